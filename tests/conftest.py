@@ -1,0 +1,65 @@
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+    config.addinivalue_line("markers", "slow: long-running CPU check")
+
+
+def _ensure_built():
+    libs = [os.path.join(ROOT, "oracle", "liboracle.so"), os.path.join(ROOT, "synth", "libsynth.so"),
+            ]
+    if not all(os.path.exists(p) for p in libs):
+        import __graft_entry__
+        __graft_entry__.build()
+
+
+_ensure_built()
+
+
+def read_golden(name):
+    """Parse `key = value` lines; repeated keys collect into lists."""
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            k, v = (s.strip() for s in line.split("=", 1))
+            out.setdefault(k, []).append(v)
+    return out
+
+
+def parse_int(tok):
+    return int(tok, 0)
+
+
+@pytest.fixture(scope="session")
+def native_checks(tmp_path_factory):
+    """Compile tests/native/exhaustive.c (a driver that calls the oracle's
+    exported step functions) into a session temp dir."""
+    import ctypes
+    src = os.path.join(ROOT, "tests", "native", "exhaustive.c")
+    out = str(tmp_path_factory.mktemp("native") / "libexhaustive.so")
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-shared", "-fPIC", src, "-o", out,
+                           "-ldl", "-lpthread"])
+    lib = ctypes.CDLL(out)
+    return lib
+
+
+def gpu_available():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
