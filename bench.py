@@ -1,0 +1,288 @@
+#!/usr/bin/env python3
+"""Benchmark: decode + dequant of one 70B-shaped transformer block on one GPU.
+
+Workload (the block the metric is quoted on): q, o 8192x8192; k, v 1024x8192;
+gate, up 28672x8192; down 8192x28672 -- 855,638,016 int8 weights whose codes
+are a 2.1-bit discrete Laplace, one 12-bit frequency table per tensor, fp32
+per-row scales, 4 super-weight escapes in down, container v1 with 64 Ki-symbol
+chunks and lane run 8. A step is one eq_decode_dequant_bf16 call over the
+whole block (one kernel launch) into a 1.71 GB bf16 buffer; containers are
+resident in HBM before timing starts.
+
+Prints one JSON line. `--workload model80` instead runs the 80-block
+double-buffered decode + GEMV schedule and prints its own line.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def host_cores() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def algorithmic_bytes(conts) -> tuple[int, int]:
+    """(compressed bytes a decode must read, bf16 bytes it must write): words
+    actually stored, lane states, chunk directory, frequency table, scales and
+    side list; 2 bytes per output weight."""
+    import numpy as np
+    comp = 0
+    n = 0
+    for c in conts:
+        h = c.hdr
+        dirs = c.host[h.off_dir:h.off_dir + 16 * h.n_chunks].reshape(-1, 16)
+        words = int(dirs[:, 8:12].copy().view(np.uint32).astype(np.int64).sum())
+        comp += 2 * words + 256 * h.n_chunks + 16 * h.n_chunks + 512 + 4 * h.rows + 10 * h.n_esc
+        n += h.n
+    return comp, 2 * n
+
+
+def traffic_record(kernel_src: str):
+    """HBM bytes per launch measured with rocprofv3 counters, if they were
+    taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "decode_block70b_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        line = line.split("#", 1)[0].strip()
+        if "=" in line:
+            k, v = (s.strip() for s in line.split("=", 1))
+            rec[k] = v
+    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    if rec.get("kernel_source_sha256") != sha:
+        return None
+    try:
+        return int(float(rec["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def build_block(cfg: int, layer: int = 0):
+    import synth
+    from rans_decode_amd import eq
+    specs = synth.config_specs(cfg)
+    conts, tensors = [], []
+    for i, sp in enumerate(specs):
+        t = synth.make_tensor(cfg, layer, i)
+        tab = eq.build_tables(t.symbols)
+        esc = t.esc_idx.size > 0
+        blob = eq.encode_host(tab, sp.dtype, sp.rows, sp.cols, t.symbols, t.scales,
+                              t.esc_idx if esc else None, t.esc_val if esc else None,
+                              esc_code=t.esc_code if esc else 0,
+                              chunk_symbols=synth.CHUNK_SYMBOLS, lane_run=synth.LANE_RUN)
+        conts.append(eq.DeviceContainer(blob, device="cuda"))
+        tensors.append(t)
+    return specs, conts, tensors
+
+
+def sampled_parity(specs, conts, tensors, out, offs, rng_seed=1) -> int:
+    """Compare a few whole chunks per tensor with the oracle; returns the
+    number of mismatching elements."""
+    import numpy as np
+    import torch
+    import oracle
+    rng = np.random.default_rng(rng_seed)
+    bad = 0
+    for sp, c, t, o in zip(specs, conts, tensors, offs):
+        nch = int(c.hdr.n_chunks)
+        for k in sorted(set(rng.integers(0, nch, 3).tolist() + [0, nch - 1])):
+            lo = k * int(c.hdr.chunk_symbols)
+            hi = min(sp.n, lo + int(c.hdr.chunk_symbols))
+            rows = slice(lo // sp.cols, (hi - 1) // sp.cols + 1)
+            sym = t.symbols[lo:hi]
+            # oracle on the chunk: positions lo..hi, rows of those positions
+            first_row = lo // sp.cols
+            sub_sc = t.scales[rows]
+            pad = lo - first_row * sp.cols
+            full = np.concatenate([np.zeros(pad, np.uint8), sym])
+            m = (t.esc_idx >= lo) & (t.esc_idx < hi)
+            exp = oracle.dequant_direct(sp.dtype, full, sp.cols, sub_sc,
+                                        t.esc_idx[m] - np.uint64(first_row * sp.cols),
+                                        t.esc_val[m])[pad:]
+            got = out[o + lo:o + hi].view(torch.int16).cpu().numpy().view(np.uint16)
+            bad += int((got != exp).sum())
+    return bad
+
+
+def cpu_baseline(conts, target_s: float = 10.0):
+    """The oracle, as it stands, decoding + dequantising a bounded sample of
+    the same containers on the host cores (chunk-parallel)."""
+    import numpy as np
+    import oracle
+    threads = host_cores()
+    sample = [(c, min(int(c.hdr.n_chunks), threads)) for c in conts]  # calibration: 1 chunk/thread
+    outs = [np.zeros(int(c.hdr.n), np.uint16) for c in conts]
+
+    def run(per_tensor):
+        t0 = time.perf_counter()
+        n = 0
+        for (c, _), k, o in zip(sample, per_tensor, outs):
+            flags = oracle.decode_chunks(c.host, 0, k, threads, bf16_out=o)
+            if flags:
+                raise RuntimeError(f"oracle decode flags {flags}")
+            n += min(int(c.hdr.n), k * int(c.hdr.chunk_symbols))
+        return time.perf_counter() - t0, n
+
+    dt, n = run([k for _, k in sample])
+    scale = max(1.0, target_s / max(dt, 1e-3))
+    ks = [min(int(c.hdr.n_chunks), max(1, int(k * scale))) for c, k in sample]
+    dt, n = run(ks)
+    desc = (f"chunks [0, k) of each of the 7 tensors, k = {ks}: {n} weights "
+            f"({n / 1e6:.1f} M), decoded + dequantised to bf16 by the oracle with {threads} threads")
+    return {"value": round(2.0 * n / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": desc, "seconds": round(dt, 2)}
+
+
+def copy_ceiling(nbytes: int) -> float:
+    """GB/s (read + write) of a plain device-to-device copy of nbytes."""
+    import torch
+    a = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    reps = 10
+    for _ in range(reps):
+        b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    del a, b
+    return 2.0 * nbytes / (ms * 1e-3) / 1e9
+
+
+def bench_block(args):
+    import numpy as np
+    import torch
+    import synth
+    from rans_decode_amd import eq
+
+    t0 = time.perf_counter()
+    specs, conts, tensors = build_block(4)
+    offs = synth.block_offsets(specs)
+    n = offs[-1]
+    log(f"block built in {time.perf_counter() - t0:.1f} s: {n} weights, "
+        f"{sum(c.nbytes for c in conts) / 1e6:.1f} MB of containers")
+    out = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    block = eq.Block(conts, offs[:-1], status)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        eq.eq_decode_dequant_bf16(block, out, stream)
+    torch.cuda.synchronize()
+    if int(status.item()) != 0:
+        raise RuntimeError(f"device status {int(status.item())}")
+    bad = sampled_parity(specs, conts, tensors, out, offs[:-1])
+    log(f"sampled parity vs oracle: {bad} mismatching elements")
+    if bad:
+        raise RuntimeError("decoded output differs from the oracle")
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for s, e in evs:
+        s.record(stream)
+        eq.eq_decode_dequant_bf16(block, out, stream)
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = [s.elapsed_time(e) for s, e in evs]
+    if int(status.item()) != 0:
+        raise RuntimeError(f"device status {int(status.item())}")
+    avg_ms = float(np.mean(ms))
+    comp, outb = algorithmic_bytes(conts)
+    algo = comp + outb
+    achieved = algo / (avg_ms * 1e-3) / 1e9
+    traffic = traffic_record(os.path.join(ROOT, "rans_decode_amd", "csrc", "decode.hip"))
+    total_container = sum(c.nbytes for c in conts)
+    rec = {
+        "metric": "decoded weight GB/s (bf16 out) and % HBM roofline, 70B-shaped block decode",
+        "value": round(outb / (avg_ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32/f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "70B-shaped block decode+dequant: q,o 8192x8192; k,v 1024x8192; "
+                        "gate,up 28672x8192; down 8192x28672; int8 2.1-bit Laplace codes, "
+                        "64Ki-symbol chunks, 64 lanes, K=8, 4 super-weight escapes, bf16 out",
+            "weights": n,
+            "container_bytes": total_container,
+            "effective_bits_per_weight": round(8.0 * total_container / n, 4),
+            "algorithmic_bytes_per_launch": algo,
+            "parallelism": "1 GPU",
+        },
+        "kernel_ms": {"mean": round(avg_ms, 4), "median": round(float(np.median(ms)), 4),
+                      "min": round(float(np.min(ms)), 4)},
+        "compressed_read_GBps": round(comp / (avg_ms * 1e-3) / 1e9, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic},
+    }
+    if not args.no_copy_ceiling:
+        cc = copy_ceiling(algo)
+        rec["copy_ceiling_GBps"] = round(cc, 1)
+        rec["frac_of_copy_ceiling"] = round(achieved / cc, 4)
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(conts, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+def bench_model(args):
+    raise SystemExit("model80 workload: not built yet")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", choices=["block70b", "model80"], default="block70b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-copy-ceiling", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this decoder has no multi-GPU path "
+              "(chunks are independent; a sharded model decodes each GPU's shard alone). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.workload == "block70b":
+        bench_block(args)
+    else:
+        bench_model(args)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,252 @@
+/*
+ * eq.h -- C ABI of libeq.so: entropy-coded Int8 / Float8 weight streams,
+ * decoded on an MI355X (gfx950) into bf16 weight buffers.
+ *
+ * The operation, as the pages state it ("Float8@2bits: Entropy Coding Enables
+ * Data-Free Model Compression", EntQuant technical summary, section 2):
+ *  - core concept: weights keep an Int8 or Float8 base format, are made
+ *    low-entropy, and are compressed losslessly with an ANS coder;
+ *  - technical component 1: per-channel scaling parameters S;
+ *  - technical component 2 (weight encoding): the weights are flattened into
+ *    one symbol stream and ANS-compressed; what is stored is the compressed
+ *    bitstream, the scales and metadata;
+ *  - technical component 3 (inference-time decoding): the bitstream stays in
+ *    GPU memory and, just before each transformer block runs, a parallel ANS
+ *    decoder expands that block's weights into a buffer;
+ *  - technical component 4 (super weights): extreme outliers are excluded
+ *    from the entropy-optimised stream (Int8 base format).
+ * "EntroLLM: Entropy Encoded Weight Compression for Efficient Large Language
+ * Model Inference on Edge Devices", technical overview, method item 3: the
+ * coded parameter space is split into chunks that keep the tensor structure
+ * and are decoded independently and concurrently.
+ *
+ * So: byte symbols + a frequency table + per-row fp32 scales in, a bf16
+ * [rows, cols] weight matrix out, with
+ *     out[i] = bf16_RNE( fp32( value(sym[i]) * S[i / cols] ) )
+ * (value: two's-complement int8, or OCP E4M3FN), and each super weight's
+ * stored bf16 bits written over its position.
+ *
+ * CONTAINER v1 (one per tensor; little-endian; the pages fix no bit-level
+ * choice, so this layout is this library's own):
+ *  - static rANS over the 256 byte codes; 12-bit frequencies (sum 4096);
+ *    u32 state in [2^16, 2^32); 16-bit renormalisation words;
+ *  - the tensor's row-major symbol stream is cut into chunks of Z symbols
+ *    (Z a multiple of 64*K; the last chunk may be shorter); each chunk is
+ *    coded by 64 interleaved lanes: at step t lane j codes chunk position
+ *    (t / K) * 64K + j * K + (t mod K), so K consecutive steps of one lane
+ *    produce K consecutive symbols (the lane run K is 1, 2, 4, 8 or 16);
+ *  - within a chunk, words are read in order of increasing step and, within
+ *    a step, increasing lane among the lanes whose state fell below 2^16;
+ *    each chunk stores its 64 final encoder states, which are the decoder's
+ *    start states; a lane with no symbols stores 2^16;
+ *  - header (256 bytes): 0 u32 magic "EQR1", 4 u16 version 1, 6 u8 dtype,
+ *    7 u8 flags (bit 0: super-weight escapes), 8 u64 rows, 16 u64 cols,
+ *    24 u64 n, 32 u32 Z, 36 u32 K, 40 u32 lanes (64), 44 u32 probability bits
+ *    (12), 48 u64 n_chunks, 56 u64 n_esc, 64 u8 escape code, 72 u64 n_words,
+ *    80..136 u64 byte offsets of: freq, scales, dir, states, words, esc_idx,
+ *    esc_val, then total size; the rest zero;
+ *  - sections, each at a 256-byte boundary: freq[256] u16 | scales[rows] f32 |
+ *    dir[n_chunks] {u64 first word, u32 word count, u32 0} | states
+ *    [n_chunks][64] u32 | words u16 (each chunk padded with zeros to a
+ *    multiple of 8 words) | esc_idx[n_esc] u64 ascending | esc_val[n_esc] u16.
+ *  - frequency quantiser (eq_build_tables): f_s = max(1, floor(c_s*4096/N))
+ *    for present bytes; the shortfall goes +1 each to the present bytes with
+ *    the largest (c_s*4096) mod N (ties: smaller byte); an excess is taken -1
+ *    at a time from the largest f_s > 1 (ties: smaller byte).
+ *  - super weights: the stream holds the escape code exactly at the listed
+ *    flat indices (the code is coded like any symbol); decode writes the
+ *    listed bf16 bits there.
+ *
+ * CONVENTIONS
+ *  - Every function returns an eq_status; no exception crosses the ABI.
+ *  - Ownership: the caller owns every host and device buffer. Decode calls
+ *    never allocate, free or synchronise: they only enqueue kernels on the
+ *    given stream (a hipStream_t passed as void*; NULL = the null stream).
+ *  - Device errors found while decoding are ORed into *d_status as
+ *    EQ_DEV_* bits; read them after synchronising. After such an error the
+ *    output contents are unspecified.
+ *  - Thread-safe and reentrant; no global mutable state.
+ */
+#ifndef EQ_H
+#define EQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t eq_status;
+#define EQ_OK 0
+#define EQ_EINVAL (-1)       /* bad argument (NULL, size, unsupported value) */
+#define EQ_ERANGE (-2)       /* output buffer too small; *out_len holds the size */
+#define EQ_ECORRUPT (-3)     /* container header or tables inconsistent */
+#define EQ_EHIP (-4)         /* HIP launch / runtime error */
+#define EQ_EUNSUPPORTED (-5) /* valid container this build cannot decode */
+#define EQ_ENOMEM (-6)       /* host allocation failed (encoder scratch) */
+
+/* Device status bits (ORed into eq_block.d_status). */
+#define EQ_DEV_BAD_END_STATE 1u /* a lane did not end at 2^16, or words left over */
+#define EQ_DEV_WORD_OVERRUN 2u  /* a chunk read past its word count / bad dir entry */
+
+#define EQ_DTYPE_INT8 1u /* two's-complement int8 codes */
+#define EQ_DTYPE_E4M3 2u /* OCP FP8 E4M3FN codes */
+
+#define EQ_LANES 64u
+#define EQ_MAX_BLOCK_TENSORS 16u /* tensors per kernel launch (more: several launches) */
+
+/* Frequency table of one tensor. */
+typedef struct eq_tables {
+    uint64_t counts[256]; /* histogram of the symbols */
+    uint64_t n;           /* number of symbols */
+    uint16_t freq[256];   /* quantised frequencies, sum 4096 */
+    uint32_t cum[257];    /* cum[s] = sum of freq[t] for t < s; cum[256] = 4096 */
+} eq_tables;
+
+/* What eq_encode_host is asked to produce. */
+typedef struct eq_tensor_desc {
+    uint32_t dtype;         /* EQ_DTYPE_INT8 or EQ_DTYPE_E4M3 */
+    uint32_t lane_run;      /* K: 1, 2, 4, 8 or 16 */
+    uint64_t rows, cols;    /* [rows, cols] row-major, rows = output channels */
+    uint32_t chunk_symbols; /* Z: multiple of 64*K, at most 2^24 */
+    uint32_t esc_enabled;   /* 1: stream carries super-weight escapes */
+    uint32_t esc_code;      /* the escape byte (used when esc_enabled) */
+    uint32_t reserved;      /* 0 */
+} eq_tensor_desc;
+
+/* Parsed, validated container header (host copy). */
+typedef struct eq_header {
+    uint32_t dtype, flags, chunk_symbols, lane_run;
+    uint64_t rows, cols, n, n_chunks, n_esc, n_words;
+    uint32_t esc_code;
+    int32_t single_symbol; /* byte of a one-symbol tensor (f = 4096), else -1 */
+    uint64_t off_freq, off_scales, off_dir, off_states, off_words, off_esc_idx, off_esc_val;
+    uint64_t total_bytes;
+} eq_header;
+
+/* One tensor of a block: its container in device memory and where its
+ * output goes. */
+typedef struct eq_tensor_ref {
+    const void *d_container; /* device pointer, 16-byte aligned, immutable while decoding */
+    eq_header hdr;           /* from eq_parse_header on the same bytes */
+    uint64_t out_offset;     /* element offset of this tensor in the output buffer */
+} eq_tensor_ref;
+
+/* A set of tensors decoded by one call (e.g. a transformer block's q, k, v,
+ * o, gate, up, down into one buffer). */
+typedef struct eq_block {
+    uint32_t n_tensors;             /* 0 is allowed (nothing is enqueued) */
+    uint32_t reserved;              /* 0 */
+    const eq_tensor_ref *tensors;   /* host array of n_tensors */
+    uint32_t *d_status;             /* device u32, caller-zeroed; may be NULL */
+} eq_block;
+
+/*
+ * eq_build_tables -- histogram + 12-bit frequency quantiser (the container's
+ * "metadata", technical component 2 of the EntQuant summary).
+ * symbols: host array of n byte codes (escape codes included). out: caller's.
+ * Errors: EQ_EINVAL if symbols/out is NULL, n == 0 or n >= 2^51.
+ */
+eq_status eq_build_tables(const uint8_t *symbols, uint64_t n, eq_tables *out);
+
+/*
+ * eq_encode_host -- offline ANS encoding of one tensor into container v1
+ * (technical component 2 of the EntQuant summary: flatten, ANS-compress,
+ * store bitstream + scales + metadata). Host only, multi-threaded over chunks.
+ * t: tables whose freq covers every symbol present (eq_build_tables output or
+ *    any valid table); d: shape and layout; symbols: rows*cols bytes; scales:
+ *    rows finite fp32; esc_idx / esc_bf16: n_esc strictly ascending flat
+ *    indices and their bf16 bits (NULL when n_esc == 0).
+ * out / cap: caller's buffer. If out is NULL or cap is too small the call
+ *    returns EQ_ERANGE with *out_len = the exact container size; on success
+ *    *out_len = bytes written.
+ * Errors (EQ_EINVAL): a symbol with frequency 0; freq not summing to 4096;
+ *    an escape list that does not match the escape-code positions (or
+ *    escapes without esc_enabled); an E4M3 NaN code outside the escapes; a
+ *    non-finite scale; K not in {1,2,4,8,16}; Z not a multiple of 64*K or
+ *    above 2^24; rows or cols 0. EQ_ENOMEM if scratch allocation fails.
+ */
+eq_status eq_encode_host(const eq_tables *t, const eq_tensor_desc *d, const uint8_t *symbols,
+                         const float *scales, const uint64_t *esc_idx, const uint16_t *esc_bf16,
+                         uint64_t n_esc, void *out, uint64_t cap, uint64_t *out_len);
+
+/*
+ * eq_parse_header -- full host-side validation of a container (header,
+ * section bounds and alignment, frequency sum, chunk directory, escape list)
+ * and extraction of its header. bytes: host copy of the whole container.
+ * Errors: EQ_EINVAL (NULL), EQ_ECORRUPT (any inconsistency).
+ */
+eq_status eq_parse_header(const void *bytes, uint64_t len, eq_header *out);
+
+/*
+ * eq_decode_block -- enqueue the parallel ANS decode of every tensor in b
+ * (technical component 3 of the EntQuant summary; chunks decoded
+ * concurrently as in EntroLLM's method item 3), writing the raw byte codes
+ * (escape codes included) to d_symbols + tensor.out_offset.
+ * d_symbols: device buffer of u8. stream: hipStream_t or NULL.
+ * Errors: EQ_EINVAL (NULL pointers, header/offset inconsistencies),
+ * EQ_EHIP (launch failure). Device-side integrity flags go to b->d_status.
+ */
+eq_status eq_decode_block(const eq_block *b, uint8_t *d_symbols, void *stream);
+
+/*
+ * eq_decode_dequant_bf16 -- enqueue decode + per-row dequantisation + bf16
+ * rounding (RNE) + super-weight patch for every tensor in b, into the bf16
+ * buffer d_bf16 (u16 bit patterns) at each tensor's out_offset: the
+ * decompression into a buffer just before a block's forward pass
+ * (technical component 3 of the EntQuant summary), with the per-channel
+ * scales of technical component 1 and the super weights of component 4.
+ * Errors: as eq_decode_block.
+ */
+eq_status eq_decode_dequant_bf16(const eq_block *b, uint16_t *d_bf16, void *stream);
+
+/*
+ * eq_gemv_bf16 -- y[r] = sum_c W[r, c] * x[c] for a row-major bf16 [rows,
+ * cols] matrix W and bf16 vector x, fp32 accumulation, fp32 y. The batch-1
+ * forward consumer of a decoded buffer (the "forward kernels" that follow
+ * the decompression, technical component 3 of the EntQuant summary). Not
+ * bit-reproducible against other summation orders.
+ * All pointers are device pointers; cols must be a multiple of 8 and W, x
+ * 16-byte aligned. Errors: EQ_EINVAL, EQ_EHIP.
+ */
+eq_status eq_gemv_bf16(const uint16_t *d_w, uint64_t rows, uint64_t cols, const uint16_t *d_x,
+                       float *d_y, void *stream);
+
+/*
+ * Block-by-block schedule (technical component 3 of the EntQuant summary:
+ * decompression interleaved with the forward kernels, block by block, into a
+ * buffer): n_blocks blocks are decoded in order into two alternating bf16
+ * buffers on decode_stream while gemv_stream runs each decoded block's
+ * GEMVs on the other buffer; events gate buffer reuse.
+ *
+ * eq_pipeline_create makes a plan holding 2 * n_blocks + 2 HIP events (no
+ * device memory). eq_pipeline_run enqueues one pass: for block b, decode into
+ * buf[b % 2] after the GEMVs of block b - 2 finished, then the GEMVs of
+ * block b (tensor i: W = buf[b % 2] + tensors[i].out_offset, rows/cols from
+ * its header, x = d_x[b][i], y = d_y[b][i]) after that decode. The run ends
+ * with gemv_stream waiting for nothing else; the caller synchronises.
+ * d_x / d_y: host arrays of n_blocks pointers to host arrays of device
+ * pointers (one per tensor). Errors: EQ_EINVAL, EQ_EHIP.
+ */
+typedef struct eq_pipeline eq_pipeline;
+eq_status eq_pipeline_create(uint32_t n_blocks, eq_pipeline **out);
+eq_status eq_pipeline_run(eq_pipeline *p, const eq_block *blocks, uint32_t n_blocks,
+                          uint16_t *d_buf0, uint16_t *d_buf1, const uint16_t *const *const *d_x,
+                          float *const *const *d_y, void *decode_stream, void *gemv_stream);
+eq_status eq_pipeline_destroy(eq_pipeline *p);
+
+/*
+ * eq_bf16_from_f32 -- diagnostic: the decode kernel's own fp32 -> bf16
+ * rounding applied to n values (device pointers), so that the rounding can be
+ * checked over all 2^32 inputs. Errors: EQ_EINVAL, EQ_EHIP.
+ */
+eq_status eq_bf16_from_f32(const float *d_in, uint64_t n, uint16_t *d_out, void *stream);
+
+/* Static text for a status code. */
+const char *eq_status_string(eq_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EQ_H */

@@ -1,0 +1,723 @@
+// decode.hip -- gfx950 (CDNA4, wave64) kernels of libeq and their launchers.
+//
+// What runs here is the inference-time half of EntQuant ("Float8@2bits:
+// Entropy Coding Enables Data-Free Model Compression", technical summary,
+// section 2): the ANS-compressed weights stay in GPU memory and, just before a
+// transformer block runs, a parallel ANS decoder expands them into a buffer
+// (technical component 3), multiplying by the per-channel scales S
+// (technical component 1) and restoring the super weights kept out of the
+// coded stream (technical component 4). Chunks are independent, as in
+// EntroLLM's parallel decoding ("EntroLLM: Entropy Encoded Weight Compression
+// for Efficient Large Language Model Inference on Edge Devices", technical
+// overview, method item 3).
+//
+// Mapping to the hardware:
+//  * one wave64 decodes one chunk; its 64 lanes are the container's 64
+//    interleaved rANS states, so a decode step is one instruction stream with
+//    no divergence;
+//  * a workgroup of 8 waves decodes 8 chunks of one tensor and shares one
+//    4096-entry slot table in LDS (4 bytes per entry: symbol byte, frequency,
+//    slot - cumulative frequency);
+//  * renormalisation words are read in the container's order with a wave
+//    ballot of the lanes that need a word plus a masked popcount (mbcnt) of
+//    the lanes below, from a per-wave LDS ring that is refilled 1 KiB at a
+//    time with 16-byte coalesced loads;
+//  * after K steps each lane holds K consecutive outputs: the fp32 scale
+//    multiply, the RNE bf16 conversion (v_cvt_pk_bf16_f32) and one 16-byte
+//    store per lane (K = 8), i.e. a 1 KiB contiguous store per wave.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <vector>
+
+#include "../../include/eq.h"
+#include "format.hpp"
+
+namespace {
+
+constexpr int kWaves = 8;                  // chunks (waves) per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr uint32_t kRing = 1024;           // renormalisation-word ring per wave (power of 2)
+constexpr uint32_t kRingAlloc = kRing + 64;  // + copy of the ring's first 64 words
+constexpr uint32_t kBlk = 512;             // words per ring refill: 16 bytes per lane
+
+enum : uint32_t {
+    F_FAST = 1u,   // aligned vector stores + (bf16) at most two rows per 64K group
+    F_CONST = 2u,  // one-symbol tensor (frequency 4096): nothing to decode
+};
+
+struct TArgs {
+    const uint8_t *base;  // container (device)
+    uint64_t out_offset, n, cols, rows, n_chunks, n_words, n_esc;
+    uint64_t off_scales, off_dir, off_states, off_words, off_esc_idx, off_esc_val, off_freq;
+    uint32_t Z, dtype, flags, const_sym;
+    uint32_t wg_begin, pad;
+};
+
+struct LArgs {
+    TArgs t[EQ_MAX_BLOCK_TENSORS];
+    void *out;
+    uint32_t *status;
+    uint32_t n_tensors;
+    uint32_t pad;
+};
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> two bf16 (round to nearest even, gradual underflow), packed.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    floatx2 f = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
+// Value of the symbol byte held in bits 0..7 of a slot-table entry.
+template <uint32_t DT>
+__device__ __forceinline__ float sym_value(uint32_t ent) {
+    if constexpr (DT == EQ_DTYPE_INT8) {
+        return (float)(int32_t)(int8_t)(ent & 0xFFu);
+    } else {
+        return __builtin_amdgcn_cvt_f32_fp8((int)ent, 0);  // OCP E4M3FN on gfx950
+    }
+}
+
+__device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
+
+__device__ __forceinline__ void raise_flag(uint32_t *status, uint32_t bits, uint32_t lane) {
+    if (status && bits && lane == 0) atomicOr(status, bits);
+}
+
+// Slot table of the tensor: for every slot in [0, 4096) the byte s with
+// cum[s] <= slot < cum[s] + f[s], packed as s | f << 8 | (slot - cum[s]) << 20
+// (f <= 4095 here; a one-symbol tensor never builds a table).
+__device__ void build_lut(const TArgs &T, uint32_t *lut, uint32_t *cum) {
+    const uint16_t *freq = reinterpret_cast<const uint16_t *>(T.base + T.off_freq);
+    const uint32_t tid = threadIdx.x;
+    if (tid < 64) {
+        uint32_t f[4];
+        uint32_t s = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[i] = freq[4 * tid + i];
+            s += f[i];
+        }
+        uint32_t incl = s;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t v = __shfl_up(incl, o, 64);
+            if (tid >= (uint32_t)o) incl += v;
+        }
+        uint32_t c = incl - s;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            cum[4 * tid + i] = c;
+            c += f[i];
+        }
+        if (tid == 63) cum[256] = incl;
+    }
+    __syncthreads();
+    for (uint32_t slot = tid; slot < 4096u; slot += kThreads) {
+        uint32_t lo = 0, hi = 256;  // cum[lo] <= slot < cum[hi]
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const uint32_t mid = (lo + hi) >> 1;
+            if (cum[mid] <= slot) lo = mid; else hi = mid;
+        }
+        const uint32_t f = cum[lo + 1] - cum[lo];
+        lut[slot] = lo | (f << 8) | ((slot - cum[lo]) << 20);
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ uint4 load_block(const uint16_t *words, uint32_t b, uint32_t wpad,
+                                            uint32_t lane) {
+    const uint32_t w0 = b * kBlk + lane * 8u;
+    uint4 v = {0u, 0u, 0u, 0u};
+    if (w0 < wpad) v = *reinterpret_cast<const uint4 *>(words + w0);
+    return v;
+}
+
+// Block b lands at ring position (b * 512) mod R; the block written at 0 is
+// also copied to [R, R + 64) so that a read at (ptr mod R) + rank, rank < 64,
+// never has to wrap.
+__device__ __forceinline__ void put_block(uint16_t *ring, uint32_t b, uint4 v, uint32_t lane) {
+    const uint32_t pos = (b * kBlk) & (kRing - 1u);
+    *reinterpret_cast<uint4 *>(ring + pos + lane * 8u) = v;
+    if (pos == 0 && lane < 8u) *reinterpret_cast<uint4 *>(ring + kRing + lane * 8u) = v;
+}
+
+// Per-chunk decoder state of one wave.
+template <int K, bool BF16, uint32_t DT, bool FAST>
+struct Chunk {
+    const TArgs &T;
+    const uint32_t *lut;
+    uint16_t *ring;
+    uint32_t lane;
+    uint64_t p0;   // flat position of the chunk's first symbol
+    uint32_t nk;   // symbols in the chunk
+    uint32_t wc, wpad, nblocks, nb;
+    const uint16_t *words;
+    uint4 pend;
+    uint32_t x;    // this lane's rANS state
+    uint32_t ptr;  // words consumed (wave-uniform)
+    uint64_t row_base, col_base;  // row / column of the current group's first symbol
+    float s_cur, s_next;          // scales of rows row_base and row_base + 1
+    uint64_t esc_i, esc_pos;
+
+    static constexpr uint32_t G = 64u * K;  // symbols per group of K steps
+
+    // Keep at least 512 staged words ahead of ptr (one group of K <= 8 steps,
+    // or half of a K = 16 group, reads at most 512 words).
+    __device__ __forceinline__ void refill() {
+        if (nb < nblocks && (int32_t)(nb * kBlk - ptr) < (int32_t)kBlk) {
+            put_block(ring, nb, pend, lane);
+            ++nb;
+            if (nb < nblocks) pend = load_block(words, nb, wpad, lane);
+        }
+    }
+
+    // One decode step of this lane (inactive lanes keep their state, which is
+    // >= 2^16, so they never ask for a word).
+    template <bool MASKED>
+    __device__ __forceinline__ uint32_t step(bool active) {
+        const uint32_t ent = lut[x & 4095u];
+        uint32_t xn = __umul24((ent >> 8) & 0xFFFu, x >> 12) + (ent >> 20);
+        if (MASKED) xn = active ? xn : x;
+        const bool need = xn < 65536u;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(need);
+        if (need) {
+            const uint32_t rank = __builtin_amdgcn_mbcnt_hi(
+                (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            xn = (xn << 16) | ring[(ptr & (kRing - 1u)) + rank];
+        }
+        ptr += (uint32_t)__builtin_popcountll(m);
+        x = xn;
+        return ent;
+    }
+
+    // The K outputs of this lane for group g, then patches and store.
+    template <bool MASKED>
+    __device__ __forceinline__ void group(uint32_t g, void *out) {
+        const uint32_t q0 = g * G + lane * (uint32_t)K;  // chunk-local first position
+        uint32_t ent[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            if ((k & 7) == 0) refill();
+            ent[k] = step<MASKED>(q0 + (uint32_t)k < nk);
+        }
+        const uint64_t g0 = p0 + (uint64_t)g * G;  // flat position of the group
+        if constexpr (BF16) {
+            uint16_t *ob = static_cast<uint16_t *>(out) + T.out_offset;
+            if constexpr (FAST) {
+                if (!MASKED) {
+                    // lanes below b are in row_base, the others in row_base + 1
+                    const uint64_t b64 = (T.cols - col_base) / (uint32_t)K;
+                    const uint32_t b = b64 < 64u ? (uint32_t)b64 : 64u;
+                    const float s = lane < b ? s_cur : s_next;
+                    uint32_t pk[(K + 1) / 2];
+#pragma unroll
+                    for (int k = 0; k < K; k += 2) {
+                        const float v0 = sym_value<DT>(ent[k]) * s;
+                        const float v1 = (k + 1 < K) ? sym_value<DT>(ent[k + 1]) * s : 0.0f;
+                        pk[k / 2] = pack_bf16(v0, v1);
+                    }
+                    patch_packed(g0, pk);
+                    store_packed(ob + g0 + lane * (uint32_t)K, pk);
+                    advance_row();
+                    return;
+                }
+            }
+            // general path: any shape, partial groups, unaligned output
+            const float *sc = reinterpret_cast<const float *>(T.base + T.off_scales);
+            const uint64_t *eidx = reinterpret_cast<const uint64_t *>(T.base + T.off_esc_idx);
+            const uint16_t *eval = reinterpret_cast<const uint16_t *>(T.base + T.off_esc_val);
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                if (q0 + (uint32_t)k < nk) {
+                    const uint64_t pos = p0 + q0 + (uint32_t)k;
+                    const float v = sym_value<DT>(ent[k]) * sc[pos / T.cols];
+                    uint16_t h = (uint16_t)(pack_bf16(v, 0.0f) & 0xFFFFu);
+                    ob[pos] = h;
+                }
+            }
+            // super weights of this group (never past the chunk's end): the
+            // owning lane rewrites them after its own store of that element
+            const uint64_t lim = (g0 + G < p0 + nk) ? g0 + G : p0 + nk;
+            while (esc_pos < lim) {
+                const uint32_t off = (uint32_t)(esc_pos - g0);
+                if (lane == off / (uint32_t)K) ob[esc_pos] = eval[esc_i];
+                ++esc_i;
+                esc_pos = esc_i < T.n_esc ? eidx[esc_i] : ~0ull;
+            }
+            if constexpr (FAST) advance_row();
+        } else {
+            uint8_t *ob = static_cast<uint8_t *>(out) + T.out_offset;
+            if (FAST && !MASKED) {
+                store_bytes(ob + g0 + lane * (uint32_t)K, ent);
+            } else {
+#pragma unroll
+                for (int k = 0; k < K; ++k)
+                    if (q0 + (uint32_t)k < nk) ob[p0 + q0 + (uint32_t)k] = (uint8_t)ent[k];
+            }
+        }
+    }
+
+    // Scales of rows row_base and row_base + 1 (the last row repeats),
+    // read through the constant address space so they are scalar loads; they
+    // change only when a group crosses into the next row.
+    __device__ __forceinline__ float row_scale(uint64_t r) const {
+        typedef const float __attribute__((address_space(4))) cfloat;
+        cfloat *sc = (cfloat *)(T.base + T.off_scales);
+        return sc[r < T.rows ? r : T.rows - 1];
+    }
+
+    __device__ __forceinline__ void advance_row() {
+        col_base += G;
+        if (col_base >= T.cols) {
+            col_base -= T.cols;
+            ++row_base;
+            s_cur = s_next;
+            s_next = row_scale(row_base + 1);
+        }
+    }
+
+    // Super weights inside this group (FAST path: fix the packed registers of
+    // the owning lane before the store).
+    __device__ __forceinline__ void patch_packed(uint64_t g0, uint32_t *pk) {
+        if (esc_pos >= g0 + G) return;
+        const uint64_t *eidx = reinterpret_cast<const uint64_t *>(T.base + T.off_esc_idx);
+        const uint16_t *eval = reinterpret_cast<const uint16_t *>(T.base + T.off_esc_val);
+        do {
+            const uint32_t off = (uint32_t)(esc_pos - g0);
+            const uint32_t owner = off / (uint32_t)K, e = off % (uint32_t)K;
+            const uint32_t v = eval[esc_i];
+            if (lane == owner) {
+#pragma unroll
+                for (int i = 0; i < (K + 1) / 2; ++i) {
+                    if (e == 2u * i) pk[i] = (pk[i] & 0xFFFF0000u) | v;
+                    if (e == 2u * i + 1u) pk[i] = (pk[i] & 0x0000FFFFu) | (v << 16);
+                }
+            }
+            ++esc_i;
+            esc_pos = esc_i < T.n_esc ? eidx[esc_i] : ~0ull;
+        } while (esc_pos < g0 + G);
+    }
+
+    __device__ __forceinline__ void store_packed(uint16_t *dst, const uint32_t *pk) {
+        if constexpr (K == 1) {
+            *dst = (uint16_t)pk[0];
+        } else if constexpr (K == 2) {
+            *reinterpret_cast<uint32_t *>(dst) = pk[0];
+        } else if constexpr (K == 4) {
+            *reinterpret_cast<uint2 *>(dst) = make_uint2(pk[0], pk[1]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < K / 8; ++i)
+                reinterpret_cast<uint4 *>(dst)[i] =
+                    make_uint4(pk[4 * i], pk[4 * i + 1], pk[4 * i + 2], pk[4 * i + 3]);
+        }
+    }
+
+    __device__ __forceinline__ void store_bytes(uint8_t *dst, const uint32_t *ent) {
+        if constexpr (K == 1) {
+            *dst = (uint8_t)ent[0];
+        } else if constexpr (K == 2) {
+            *reinterpret_cast<uint16_t *>(dst) = (uint16_t)((ent[0] & 0xFFu) | ((ent[1] & 0xFFu) << 8));
+        } else {
+            uint32_t w[K / 4];
+#pragma unroll
+            for (int i = 0; i < K / 4; ++i)
+                w[i] = (ent[4 * i] & 0xFFu) | ((ent[4 * i + 1] & 0xFFu) << 8) |
+                       ((ent[4 * i + 2] & 0xFFu) << 16) | ((ent[4 * i + 3] & 0xFFu) << 24);
+            if constexpr (K == 4) {
+                *reinterpret_cast<uint32_t *>(dst) = w[0];
+            } else if constexpr (K == 8) {
+                *reinterpret_cast<uint2 *>(dst) = make_uint2(w[0], w[1]);
+            } else {
+                *reinterpret_cast<uint4 *>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
+    }
+
+    __device__ void run(uint64_t chunk, void *out, uint32_t *status) {
+        const uint8_t *dir = T.base + T.off_dir + chunk * 16u;
+        const uint64_t ws = *reinterpret_cast<const uint64_t *>(dir);
+        wc = *reinterpret_cast<const uint32_t *>(dir + 8);
+        wpad = (wc + 7u) & ~7u;
+        if (wc > nk || ws + wpad > T.n_words) {
+            raise_flag(status, EQ_DEV_WORD_OVERRUN, lane);
+            return;
+        }
+        words = reinterpret_cast<const uint16_t *>(T.base + T.off_words) + ws;
+        x = reinterpret_cast<const uint32_t *>(T.base + T.off_states)[chunk * 64u + lane];
+        nblocks = (wpad + kBlk - 1u) / kBlk;
+        nb = 0;
+        ptr = 0;
+        pend = make_uint4(0u, 0u, 0u, 0u);
+        if (nblocks) {
+            put_block(ring, 0, load_block(words, 0, wpad, lane), lane);
+            nb = 1;
+            if (nb < nblocks) pend = load_block(words, nb, wpad, lane);
+        }
+        row_base = p0 / T.cols;
+        col_base = p0 - row_base * T.cols;
+        if constexpr (BF16 && FAST) {
+            s_cur = row_scale(row_base);
+            s_next = row_scale(row_base + 1);
+        }
+        esc_pos = ~0ull;
+        esc_i = 0;
+        if (BF16 && T.n_esc) {
+            // first super weight at or after p0
+            const uint64_t *eidx = reinterpret_cast<const uint64_t *>(T.base + T.off_esc_idx);
+            uint64_t lo = 0, hi = T.n_esc;
+            while (lo < hi) {
+                const uint64_t mid = (lo + hi) >> 1;
+                if (eidx[mid] < p0) lo = mid + 1; else hi = mid;
+            }
+            esc_i = lo;
+            esc_pos = lo < T.n_esc ? eidx[lo] : ~0ull;
+        }
+        // settle the set-up loads here rather than at the loop header, where
+        // the wait would be repeated every group
+        __builtin_amdgcn_s_waitcnt(0);
+        const uint32_t nfull = nk / G;
+        for (uint32_t g = 0; g < nfull; ++g) group<false>(g, out);
+        if (nfull * G < nk) group<true>(nfull, out);
+
+        // integrity: every lane back at 2^16 and every word consumed
+        const uint64_t bad = __builtin_amdgcn_ballot_w64(x != 65536u);
+        uint32_t bits = 0;
+        if (ptr > wc) bits |= EQ_DEV_WORD_OVERRUN;
+        else if (ptr != wc || bad) bits |= EQ_DEV_BAD_END_STATE;
+        raise_flag(status, bits, lane);
+    }
+};
+
+// One-symbol tensor: every state must be 2^16 and no word stored; the output
+// is the symbol's dequantised value everywhere (escapes patched).
+template <bool BF16>
+__device__ void const_chunk(const TArgs &T, uint64_t chunk, uint32_t lane, void *out,
+                            uint32_t *status) {
+    const uint64_t p0 = chunk * T.Z;
+    const uint32_t nk = (uint32_t)umin64(T.Z, T.n - p0);
+    const uint8_t *dir = T.base + T.off_dir + chunk * 16u;
+    const uint32_t wc = *reinterpret_cast<const uint32_t *>(dir + 8);
+    const uint32_t xs = reinterpret_cast<const uint32_t *>(T.base + T.off_states)[chunk * 64u + lane];
+    const uint64_t bad = __builtin_amdgcn_ballot_w64(xs != 65536u);
+    raise_flag(status, (bad || wc) ? EQ_DEV_BAD_END_STATE : 0u, lane);
+    const float *sc = reinterpret_cast<const float *>(T.base + T.off_scales);
+    for (uint32_t q = lane; q < nk; q += 64u) {
+        const uint64_t pos = p0 + q;
+        if constexpr (BF16) {
+            const float v = (T.dtype == EQ_DTYPE_INT8 ? sym_value<EQ_DTYPE_INT8>(T.const_sym)
+                                                       : sym_value<EQ_DTYPE_E4M3>(T.const_sym)) *
+                            sc[pos / T.cols];
+            static_cast<uint16_t *>(out)[T.out_offset + pos] = (uint16_t)(pack_bf16(v, 0.0f) & 0xFFFFu);
+        } else {
+            static_cast<uint8_t *>(out)[T.out_offset + pos] = (uint8_t)T.const_sym;
+        }
+    }
+    if constexpr (BF16) {
+        if (T.n_esc) {
+            // the lane that stored an element also patches it (program order)
+            const uint64_t *eidx = reinterpret_cast<const uint64_t *>(T.base + T.off_esc_idx);
+            const uint16_t *eval = reinterpret_cast<const uint16_t *>(T.base + T.off_esc_val);
+            for (uint64_t e = 0; e < T.n_esc; ++e) {
+                const uint64_t p = eidx[e];
+                if (p >= p0 && p < p0 + nk && (uint32_t)((p - p0) % 64u) == lane)
+                    static_cast<uint16_t *>(out)[T.out_offset + p] = eval[e];
+            }
+        }
+    }
+}
+
+template <int K, bool BF16>
+__global__ void __launch_bounds__(kThreads) k_decode(LArgs a) {
+    __shared__ uint32_t lut[4096];
+    __shared__ __attribute__((aligned(16))) uint16_t rings[kWaves][kRingAlloc];
+    __shared__ uint32_t cum[260];
+
+    const uint32_t wg = blockIdx.x;
+    uint32_t ti = 0;
+    while (ti + 1 < a.n_tensors && wg >= a.t[ti + 1].wg_begin) ++ti;
+    const TArgs &T = a.t[ti];
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint64_t chunk = (uint64_t)(wg - T.wg_begin) * kWaves + wave;
+    const bool is_const = (T.flags & F_CONST) != 0;
+    if (!is_const) build_lut(T, lut, cum);
+    if (chunk >= T.n_chunks) return;
+    if (is_const) {
+        const_chunk<BF16>(T, chunk, lane, a.out, a.status);
+        return;
+    }
+    const uint64_t p0 = chunk * T.Z;
+    const uint32_t nk = (uint32_t)umin64(T.Z, T.n - p0);
+    const bool fast = (T.flags & F_FAST) != 0;
+#define EQ_RUN(BF, DT, FA)                                                             \
+    do {                                                                               \
+        Chunk<K, BF, DT, FA> c{T, lut, rings[wave], lane, p0, nk};                     \
+        c.run(chunk, a.out, a.status);                                                 \
+    } while (0)
+    if constexpr (BF16) {
+        if (T.dtype == EQ_DTYPE_INT8) {
+            if (fast) EQ_RUN(true, EQ_DTYPE_INT8, true); else EQ_RUN(true, EQ_DTYPE_INT8, false);
+        } else {
+            if (fast) EQ_RUN(true, EQ_DTYPE_E4M3, true); else EQ_RUN(true, EQ_DTYPE_E4M3, false);
+        }
+    } else {
+        if (fast) EQ_RUN(false, 0u, true); else EQ_RUN(false, 0u, false);
+    }
+#undef EQ_RUN
+}
+
+// ---------------------------------------------------------------------------
+// Batch-1 bf16 GEMV (the consumer of a decoded block): one wave per row,
+// 16-byte loads, fp32 accumulation, wave reduction.
+// ---------------------------------------------------------------------------
+constexpr int kGemvWaves = 4;
+
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+__device__ __forceinline__ float dot8(uint4 w, uint4 v, float acc) {
+    acc = fmaf(bf_lo(w.x), bf_lo(v.x), acc);
+    acc = fmaf(bf_hi(w.x), bf_hi(v.x), acc);
+    acc = fmaf(bf_lo(w.y), bf_lo(v.y), acc);
+    acc = fmaf(bf_hi(w.y), bf_hi(v.y), acc);
+    acc = fmaf(bf_lo(w.z), bf_lo(v.z), acc);
+    acc = fmaf(bf_hi(w.z), bf_hi(v.z), acc);
+    acc = fmaf(bf_lo(w.w), bf_lo(v.w), acc);
+    acc = fmaf(bf_hi(w.w), bf_hi(v.w), acc);
+    return acc;
+}
+
+__global__ void __launch_bounds__(64 * kGemvWaves)
+k_gemv(const uint16_t *__restrict__ W, uint64_t rows, uint64_t cols, const uint16_t *__restrict__ xv,
+       float *__restrict__ y) {
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint64_t row = (uint64_t)blockIdx.x * kGemvWaves + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const uint16_t *w = W + row * cols;
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    uint64_t c = lane * 8u;
+    for (; c + 3 * 512 < cols; c += 4 * 512) {
+        const uint4 w0 = *reinterpret_cast<const uint4 *>(w + c);
+        const uint4 w1 = *reinterpret_cast<const uint4 *>(w + c + 512);
+        const uint4 w2 = *reinterpret_cast<const uint4 *>(w + c + 1024);
+        const uint4 w3 = *reinterpret_cast<const uint4 *>(w + c + 1536);
+        a0 = dot8(w0, *reinterpret_cast<const uint4 *>(xv + c), a0);
+        a1 = dot8(w1, *reinterpret_cast<const uint4 *>(xv + c + 512), a1);
+        a2 = dot8(w2, *reinterpret_cast<const uint4 *>(xv + c + 1024), a2);
+        a3 = dot8(w3, *reinterpret_cast<const uint4 *>(xv + c + 1536), a3);
+    }
+    for (; c < cols; c += 512)
+        a0 = dot8(*reinterpret_cast<const uint4 *>(w + c), *reinterpret_cast<const uint4 *>(xv + c), a0);
+    float acc = (a0 + a1) + (a2 + a3);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    if (lane == 0) y[row] = acc;
+}
+
+// Diagnostic: the decode kernel's fp32 -> bf16 rounding on an array.
+__global__ void k_bf16(const float *__restrict__ in, uint64_t n, uint16_t *__restrict__ out) {
+    const uint64_t i = ((uint64_t)blockIdx.x * blockDim.x + threadIdx.x) * 2u;
+    if (i + 1 < n) {
+        const uint32_t p = pack_bf16(in[i], in[i + 1]);
+        out[i] = (uint16_t)p;
+        out[i + 1] = (uint16_t)(p >> 16);
+    } else if (i < n) {
+        out[i] = (uint16_t)pack_bf16(in[i], 0.0f);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+// ---------------------------------------------------------------------------
+template <bool BF16>
+using KernelFn = void (*)(LArgs);
+
+template <bool BF16>
+KernelFn<BF16> pick_kernel(uint32_t K) {
+    switch (K) {
+        case 1: return k_decode<1, BF16>;
+        case 2: return k_decode<2, BF16>;
+        case 4: return k_decode<4, BF16>;
+        case 8: return k_decode<8, BF16>;
+        case 16: return k_decode<16, BF16>;
+        default: return nullptr;
+    }
+}
+
+// Header fields the kernel relies on, re-checked against each other.
+bool header_ok(const eq_header &h) {
+    if (h.dtype != EQ_DTYPE_INT8 && h.dtype != EQ_DTYPE_E4M3) return false;
+    if (!eqfmt::valid_lane_run(h.lane_run)) return false;
+    if (h.chunk_symbols == 0 || h.chunk_symbols > eqfmt::kMaxChunk ||
+        h.chunk_symbols % (64u * h.lane_run))
+        return false;
+    if (h.rows == 0 || h.cols == 0 || h.rows * h.cols != h.n) return false;
+    if (h.n_chunks != (h.n + h.chunk_symbols - 1) / h.chunk_symbols) return false;
+    const eqfmt::Sections s = eqfmt::layout(h.rows, h.n_chunks, h.n_words, h.n_esc);
+    return s.freq == h.off_freq && s.scales == h.off_scales && s.dir == h.off_dir &&
+           s.states == h.off_states && s.words == h.off_words && s.esc_idx == h.off_esc_idx &&
+           s.esc_val == h.off_esc_val && s.total == h.total_bytes;
+}
+
+template <bool BF16>
+eq_status launch_block(const eq_block *b, void *out, void *stream) {
+    if (!b || (b->n_tensors && !b->tensors) || (b->n_tensors && !out)) return EQ_EINVAL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uintptr_t obase = reinterpret_cast<uintptr_t>(out);
+    uint32_t i = 0;
+    while (i < b->n_tensors) {
+        LArgs a{};
+        a.out = out;
+        a.status = b->d_status;
+        const uint32_t K = b->tensors[i].hdr.lane_run;
+        uint64_t wgs = 0;
+        uint32_t nt = 0;
+        for (; i < b->n_tensors && nt < EQ_MAX_BLOCK_TENSORS; ++i, ++nt) {
+            const eq_tensor_ref &r = b->tensors[i];
+            const eq_header &h = r.hdr;
+            if (h.lane_run != K) break;
+            if (!r.d_container || (reinterpret_cast<uintptr_t>(r.d_container) & 15u)) return EQ_EINVAL;
+            if (!header_ok(h)) return EQ_EINVAL;
+            TArgs &t = a.t[nt];
+            t.base = static_cast<const uint8_t *>(r.d_container);
+            t.out_offset = r.out_offset;
+            t.n = h.n;
+            t.cols = h.cols;
+            t.rows = h.rows;
+            t.n_chunks = h.n_chunks;
+            t.n_words = h.n_words;
+            t.n_esc = h.n_esc;
+            t.off_freq = h.off_freq;
+            t.off_scales = h.off_scales;
+            t.off_dir = h.off_dir;
+            t.off_states = h.off_states;
+            t.off_words = h.off_words;
+            t.off_esc_idx = h.off_esc_idx;
+            t.off_esc_val = h.off_esc_val;
+            t.Z = h.chunk_symbols;
+            t.dtype = h.dtype;
+            t.flags = 0;
+            t.const_sym = 0;
+            if (h.single_symbol >= 0) {
+                t.flags |= F_CONST;
+                t.const_sym = (uint32_t)h.single_symbol;
+            }
+            const uint32_t vec = BF16 ? 2u * (K < 8 ? K : 8u) : K;  // bytes per store
+            const uint64_t elem = BF16 ? 2u : 1u;
+            const bool aligned = ((obase + r.out_offset * elem) % vec) == 0;
+            const bool rows_ok = !BF16 || (h.cols % K == 0 && h.cols >= 64u * K);
+            if (aligned && rows_ok) t.flags |= F_FAST;
+            t.wg_begin = (uint32_t)wgs;
+            wgs += (h.n_chunks + kWaves - 1) / kWaves;
+        }
+        a.n_tensors = nt;
+        if (wgs > 0x7FFFFFFFull) return EQ_EINVAL;
+        if (wgs) {
+            KernelFn<BF16> fn = pick_kernel<BF16>(K);
+            if (!fn) return EQ_EINVAL;
+            hipLaunchKernelGGL(fn, dim3((uint32_t)wgs), dim3(kThreads), 0, s, a);
+            if (hipGetLastError() != hipSuccess) return EQ_EHIP;
+        }
+    }
+    return EQ_OK;
+}
+
+}  // namespace
+
+struct eq_pipeline {
+    uint32_t n_blocks;
+    std::vector<hipEvent_t> decoded, consumed;
+};
+
+extern "C" {
+
+eq_status eq_decode_block(const eq_block *b, uint8_t *d_symbols, void *stream) {
+    return launch_block<false>(b, d_symbols, stream);
+}
+
+eq_status eq_decode_dequant_bf16(const eq_block *b, uint16_t *d_bf16, void *stream) {
+    return launch_block<true>(b, d_bf16, stream);
+}
+
+eq_status eq_gemv_bf16(const uint16_t *d_w, uint64_t rows, uint64_t cols, const uint16_t *d_x,
+                       float *d_y, void *stream) {
+    if (!d_w || !d_x || !d_y || rows == 0 || cols == 0 || cols % 8) return EQ_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(d_w) | reinterpret_cast<uintptr_t>(d_x)) & 15u) return EQ_EINVAL;
+    const uint64_t grid = (rows + kGemvWaves - 1) / kGemvWaves;
+    if (grid > 0x7FFFFFFFull) return EQ_EINVAL;
+    hipLaunchKernelGGL(k_gemv, dim3((uint32_t)grid), dim3(64 * kGemvWaves), 0,
+                       static_cast<hipStream_t>(stream), d_w, rows, cols, d_x, d_y);
+    return hipGetLastError() == hipSuccess ? EQ_OK : EQ_EHIP;
+}
+
+eq_status eq_bf16_from_f32(const float *d_in, uint64_t n, uint16_t *d_out, void *stream) {
+    if (!d_in || !d_out) return EQ_EINVAL;
+    if (n == 0) return EQ_OK;
+    const uint64_t threads = (n + 1) / 2;
+    const uint64_t grid = (threads + 255) / 256;
+    if (grid > 0x7FFFFFFFull) return EQ_EINVAL;
+    hipLaunchKernelGGL(k_bf16, dim3((uint32_t)grid), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), d_in, n, d_out);
+    return hipGetLastError() == hipSuccess ? EQ_OK : EQ_EHIP;
+}
+
+eq_status eq_pipeline_create(uint32_t n_blocks, eq_pipeline **out) {
+    if (!out || n_blocks == 0) return EQ_EINVAL;
+    eq_pipeline *p = new (std::nothrow) eq_pipeline;
+    if (!p) return EQ_ENOMEM;
+    p->n_blocks = n_blocks;
+    p->decoded.assign(n_blocks, nullptr);
+    p->consumed.assign(n_blocks, nullptr);
+    for (uint32_t i = 0; i < n_blocks; ++i) {
+        if (hipEventCreateWithFlags(&p->decoded[i], hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&p->consumed[i], hipEventDisableTiming) != hipSuccess) {
+            eq_pipeline_destroy(p);
+            return EQ_EHIP;
+        }
+    }
+    *out = p;
+    return EQ_OK;
+}
+
+eq_status eq_pipeline_run(eq_pipeline *p, const eq_block *blocks, uint32_t n_blocks,
+                          uint16_t *d_buf0, uint16_t *d_buf1, const uint16_t *const *const *d_x,
+                          float *const *const *d_y, void *decode_stream, void *gemv_stream) {
+    if (!p || !blocks || !d_buf0 || !d_buf1 || !d_x || !d_y || n_blocks > p->n_blocks) return EQ_EINVAL;
+    hipStream_t ds = static_cast<hipStream_t>(decode_stream);
+    hipStream_t gs = static_cast<hipStream_t>(gemv_stream);
+    uint16_t *buf[2] = {d_buf0, d_buf1};
+    for (uint32_t b = 0; b < n_blocks; ++b) {
+        uint16_t *dst = buf[b & 1u];
+        if (b >= 2 && hipStreamWaitEvent(ds, p->consumed[b - 2], 0) != hipSuccess) return EQ_EHIP;
+        eq_status st = eq_decode_dequant_bf16(&blocks[b], dst, ds);
+        if (st != EQ_OK) return st;
+        if (hipEventRecord(p->decoded[b], ds) != hipSuccess) return EQ_EHIP;
+        if (hipStreamWaitEvent(gs, p->decoded[b], 0) != hipSuccess) return EQ_EHIP;
+        if (!d_x[b] || !d_y[b]) return EQ_EINVAL;
+        for (uint32_t t = 0; t < blocks[b].n_tensors; ++t) {
+            const eq_tensor_ref &r = blocks[b].tensors[t];
+            st = eq_gemv_bf16(dst + r.out_offset, r.hdr.rows, r.hdr.cols, d_x[b][t], d_y[b][t], gs);
+            if (st != EQ_OK) return st;
+        }
+        if (hipEventRecord(p->consumed[b], gs) != hipSuccess) return EQ_EHIP;
+    }
+    return EQ_OK;
+}
+
+eq_status eq_pipeline_destroy(eq_pipeline *p) {
+    if (!p) return EQ_EINVAL;
+    for (hipEvent_t e : p->decoded)
+        if (e) (void)hipEventDestroy(e);
+    for (hipEvent_t e : p->consumed)
+        if (e) (void)hipEventDestroy(e);
+    delete p;
+    return EQ_OK;
+}
+
+}  // extern "C"

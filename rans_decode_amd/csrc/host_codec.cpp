@@ -1,0 +1,402 @@
+// host_codec.cpp -- host side of libeq: frequency tables, the offline
+// container encoder and container validation.
+//
+// The pages' encoding step ("Float8@2bits: Entropy Coding Enables Data-Free
+// Model Compression", EntQuant technical summary, section 2, technical
+// component 2): the optimised weights are flattened into a symbol stream and
+// compressed with an ANS coder; the stored artefact is the compressed
+// bitstream, the scaling parameters and metadata. The chunking follows
+// "EntroLLM: Entropy Encoded Weight Compression for Efficient Large Language
+// Model Inference on Edge Devices", technical overview, method item 3: the
+// coded parameter space is split into independent chunks that keep the
+// tensor's structure.
+#include <algorithm>
+#include <array>
+#include <atomic>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <memory>
+#include <new>
+#include <thread>
+#include <vector>
+
+#include "../../include/eq.h"
+#include "format.hpp"
+
+using namespace eqfmt;
+
+namespace {
+
+unsigned worker_count(uint64_t units) {
+    unsigned hw = std::thread::hardware_concurrency();
+    if (const char *env = std::getenv("EQ_HOST_THREADS")) hw = (unsigned)std::atoi(env);
+    if (hw == 0) hw = 1;
+    hw = std::min(hw, 64u);
+    return (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(hw, units));
+}
+
+// Run fn(i) for i in [0, count) on worker threads, handing out indices from
+// a shared counter.
+template <class F>
+void parallel_for(uint64_t count, F &&fn) {
+    unsigned nw = worker_count(count);
+    if (nw <= 1) {
+        for (uint64_t i = 0; i < count; ++i) fn(i);
+        return;
+    }
+    std::atomic<uint64_t> next{0};
+    auto body = [&] {
+        for (uint64_t i; (i = next.fetch_add(1)) < count;) fn(i);
+    };
+    std::vector<std::thread> pool;
+    pool.reserve(nw - 1);
+    for (unsigned w = 1; w < nw; ++w) pool.emplace_back(body);
+    body();
+    for (auto &t : pool) t.join();
+}
+
+inline void wr16(uint8_t *p, uint16_t v) { std::memcpy(p, &v, 2); }
+inline void wr32(uint8_t *p, uint32_t v) { std::memcpy(p, &v, 4); }
+inline void wr64(uint8_t *p, uint64_t v) { std::memcpy(p, &v, 8); }
+inline uint16_t rd16(const uint8_t *p) { uint16_t v; std::memcpy(&v, p, 2); return v; }
+inline uint32_t rd32(const uint8_t *p) { uint32_t v; std::memcpy(&v, p, 4); return v; }
+inline uint64_t rd64(const uint8_t *p) { uint64_t v; std::memcpy(&v, p, 8); return v; }
+
+// ---------------------------------------------------------------------------
+// 12-bit frequency quantiser (rule stated in include/eq.h).
+// ---------------------------------------------------------------------------
+eq_status quantise(const uint64_t counts[256], uint64_t N, uint16_t freq[256]) {
+    struct Entry {
+        int sym;
+        uint64_t rem;
+    };
+    std::vector<Entry> present;
+    int64_t f[256];
+    int64_t total = 0;
+    for (int s = 0; s < 256; ++s) {
+        f[s] = 0;
+        if (!counts[s]) continue;
+        const uint64_t scaled = counts[s] * (uint64_t)kProbScale;
+        f[s] = std::max<int64_t>(1, (int64_t)(scaled / N));
+        present.push_back({s, scaled % N});
+        total += f[s];
+    }
+    int64_t deficit = (int64_t)kProbScale - total;
+    if (deficit > 0) {
+        // hand the shortfall to the largest remainders, smaller byte first on ties
+        std::stable_sort(present.begin(), present.end(),
+                         [](const Entry &a, const Entry &b) { return a.rem > b.rem; });
+        if ((uint64_t)deficit > present.size()) return EQ_EINVAL;
+        for (int64_t i = 0; i < deficit; ++i) f[present[(size_t)i].sym] += 1;
+    } else {
+        // take the excess one at a time from the currently largest f > 1
+        for (; deficit < 0; ++deficit) {
+            int pick = -1;
+            for (int s = 255; s >= 0; --s)
+                if (f[s] > 1 && (pick < 0 || f[s] >= f[pick])) pick = s;
+            if (pick < 0) return EQ_EINVAL;
+            f[pick] -= 1;
+        }
+    }
+    for (int s = 0; s < 256; ++s) freq[s] = (uint16_t)f[s];
+    return EQ_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Chunk encoder.
+// ---------------------------------------------------------------------------
+struct SymInfo {
+    uint32_t freq;
+    uint32_t start;
+    uint64_t renorm_at;  // state at and above which one word is flushed first: freq << 20
+};
+
+// Encodes one chunk of nk symbols with 64 interleaved lanes. The symbols are
+// visited from the last (step, lane) back to the first, and each flushed
+// word is written just before the previous one, so the words come out in the
+// decoder's reading order. `wend` points one past the chunk's word region,
+// which has room for nk words (at most one word per symbol). Returns the
+// number of words; they occupy [wend - count, wend).
+uint64_t encode_chunk(const uint8_t *sym, uint32_t nk, uint32_t K, const SymInfo *tab,
+                      uint32_t *final_states, uint16_t *wend) {
+    uint32_t lane_state[kLanes];
+    for (uint32_t j = 0; j < kLanes; ++j) lane_state[j] = kStateLow;
+    uint16_t *w = wend;
+    const uint32_t group = kLanes * K;
+    const uint32_t groups = (nk + group - 1) / group;
+    for (uint32_t g = groups; g-- > 0;) {
+        const uint32_t gbase = g * group;
+        for (uint32_t r = K; r-- > 0;) {
+            for (uint32_t j = kLanes; j-- > 0;) {
+                const uint32_t pos = gbase + j * K + r;
+                if (pos >= nk) continue;
+                const SymInfo &si = tab[sym[pos]];
+                uint32_t x = lane_state[j];
+                if ((uint64_t)x >= si.renorm_at) {
+                    *--w = (uint16_t)(x & 0xFFFFu);
+                    x >>= 16;
+                }
+                const uint32_t q = x / si.freq;
+                lane_state[j] = (q << kProbBits) + (x - q * si.freq) + si.start;
+            }
+        }
+    }
+    std::memcpy(final_states, lane_state, sizeof lane_state);
+    return (uint64_t)(wend - w);
+}
+
+bool is_e4m3_nan(uint8_t c) { return (c & 0x7Fu) == 0x7Fu; }
+
+}  // namespace
+
+extern "C" {
+
+const char *eq_status_string(eq_status s) {
+    switch (s) {
+        case EQ_OK: return "ok";
+        case EQ_EINVAL: return "invalid argument";
+        case EQ_ERANGE: return "output buffer too small";
+        case EQ_ECORRUPT: return "corrupt container";
+        case EQ_EHIP: return "HIP runtime error";
+        case EQ_EUNSUPPORTED: return "unsupported";
+        case EQ_ENOMEM: return "out of host memory";
+        default: return "unknown status";
+    }
+}
+
+eq_status eq_build_tables(const uint8_t *symbols, uint64_t n, eq_tables *out) {
+    if (!symbols || !out || n == 0 || n >= (1ull << 51)) return EQ_EINVAL;
+    const uint64_t slice = 1ull << 22;
+    const uint64_t nslices = (n + slice - 1) / slice;
+    std::vector<std::array<uint64_t, 256>> part(nslices);
+    parallel_for(nslices, [&](uint64_t i) {
+        auto &h = part[i];
+        h.fill(0);
+        const uint64_t lo = i * slice, hi = std::min(n, lo + slice);
+        for (uint64_t k = lo; k < hi; ++k) h[symbols[k]]++;
+    });
+    std::memset(out, 0, sizeof *out);
+    for (const auto &h : part)
+        for (int s = 0; s < 256; ++s) out->counts[s] += h[s];
+    out->n = n;
+    eq_status st = quantise(out->counts, n, out->freq);
+    if (st != EQ_OK) return st;
+    out->cum[0] = 0;
+    for (int s = 0; s < 256; ++s) out->cum[s + 1] = out->cum[s] + out->freq[s];
+    return EQ_OK;
+}
+
+eq_status eq_encode_host(const eq_tables *t, const eq_tensor_desc *d, const uint8_t *symbols,
+                         const float *scales, const uint64_t *esc_idx, const uint16_t *esc_bf16,
+                         uint64_t n_esc, void *out, uint64_t cap, uint64_t *out_len) {
+    if (!t || !d || !symbols || !scales || !out_len) return EQ_EINVAL;
+    if (n_esc && (!esc_idx || !esc_bf16)) return EQ_EINVAL;
+    if (d->dtype != EQ_DTYPE_INT8 && d->dtype != EQ_DTYPE_E4M3) return EQ_EINVAL;
+    if (d->rows == 0 || d->cols == 0 || d->cols > (1ull << 40) / d->rows) return EQ_EINVAL;
+    if (!valid_lane_run(d->lane_run)) return EQ_EINVAL;
+    const uint32_t K = d->lane_run, Z = d->chunk_symbols;
+    if (Z == 0 || Z > kMaxChunk || Z % (kLanes * K) != 0) return EQ_EINVAL;
+    if (!d->esc_enabled && n_esc) return EQ_EINVAL;
+    if (d->esc_enabled && d->esc_code > 255) return EQ_EINVAL;
+    uint32_t fsum = 0;
+    for (int s = 0; s < 256; ++s) fsum += t->freq[s];
+    if (fsum != kProbScale) return EQ_EINVAL;
+
+    const uint64_t n = d->rows * d->cols;
+    for (uint64_t r = 0; r < d->rows; ++r)
+        if (!std::isfinite(scales[r])) return EQ_EINVAL;
+    for (uint64_t e = 0; e < n_esc; ++e) {
+        if (esc_idx[e] >= n || (e && esc_idx[e] <= esc_idx[e - 1])) return EQ_EINVAL;
+        if (symbols[esc_idx[e]] != d->esc_code) return EQ_EINVAL;
+    }
+
+    // per-slice symbol validation (frequency present, NaN codes, escape count)
+    const uint64_t slice = 1ull << 22;
+    const uint64_t nslices = (n + slice - 1) / slice;
+    std::vector<uint64_t> esc_seen(nslices, 0);
+    std::vector<uint8_t> bad(nslices, 0);
+    parallel_for(nslices, [&](uint64_t i) {
+        const uint64_t lo = i * slice, hi = std::min(n, lo + slice);
+        uint64_t seen = 0;
+        bool b = false;
+        for (uint64_t k = lo; k < hi; ++k) {
+            const uint8_t c = symbols[k];
+            b |= t->freq[c] == 0;
+            const bool is_esc = d->esc_enabled && c == d->esc_code;
+            seen += is_esc;
+            b |= d->dtype == EQ_DTYPE_E4M3 && is_e4m3_nan(c) && !is_esc;
+        }
+        esc_seen[i] = seen;
+        bad[i] = b;
+    });
+    uint64_t esc_total = 0;
+    for (uint64_t i = 0; i < nslices; ++i) {
+        if (bad[i]) return EQ_EINVAL;
+        esc_total += esc_seen[i];
+    }
+    if (esc_total != n_esc) return EQ_EINVAL;
+
+    SymInfo tab[256];
+    for (int s = 0; s < 256; ++s) {
+        tab[s].freq = t->freq[s] ? t->freq[s] : 1;
+        tab[s].start = t->cum[s];
+        tab[s].renorm_at = (uint64_t)t->freq[s] << 20;
+    }
+    {   // cum must match freq
+        uint32_t c = 0;
+        for (int s = 0; s < 256; ++s) {
+            if (t->cum[s] != c) return EQ_EINVAL;
+            c += t->freq[s];
+        }
+    }
+
+    const uint64_t n_chunks = (n + Z - 1) / Z;
+    std::unique_ptr<uint16_t[]> scratch(new (std::nothrow) uint16_t[n]);
+    std::unique_ptr<uint32_t[]> states(new (std::nothrow) uint32_t[n_chunks * kLanes]);
+    std::unique_ptr<uint64_t[]> wcount(new (std::nothrow) uint64_t[n_chunks]);
+    if (!scratch || !states || !wcount) return EQ_ENOMEM;
+
+    // chunk k encodes into scratch[k*Z, k*Z + nk), filled from its end
+    parallel_for(n_chunks, [&](uint64_t k) {
+        const uint64_t p0 = k * Z;
+        const uint32_t nk = (uint32_t)std::min<uint64_t>(Z, n - p0);
+        wcount[k] = encode_chunk(symbols + p0, nk, K, tab, &states[k * kLanes],
+                                 scratch.get() + p0 + nk);
+    });
+
+    uint64_t n_words = 0;
+    for (uint64_t k = 0; k < n_chunks; ++k) n_words += round_up(wcount[k], kWordPad);
+    const Sections sec = layout(d->rows, n_chunks, n_words, n_esc);
+    *out_len = sec.total;
+    if (!out || cap < sec.total) return EQ_ERANGE;
+
+    uint8_t *b = static_cast<uint8_t *>(out);
+    std::memset(b, 0, sec.freq);
+    wr32(b + H_MAGIC, kMagic);
+    wr16(b + H_VERSION, kVersion);
+    b[H_DTYPE] = (uint8_t)d->dtype;
+    b[H_FLAGS] = d->esc_enabled ? 1 : 0;
+    wr64(b + H_ROWS, d->rows);
+    wr64(b + H_COLS, d->cols);
+    wr64(b + H_N, n);
+    wr32(b + H_CHUNK, Z);
+    wr32(b + H_LANE_RUN, K);
+    wr32(b + H_LANES, kLanes);
+    wr32(b + H_PROB_BITS, kProbBits);
+    wr64(b + H_NCHUNKS, n_chunks);
+    wr64(b + H_NESC, n_esc);
+    b[H_ESC_CODE] = d->esc_enabled ? (uint8_t)d->esc_code : 0;
+    wr64(b + H_NWORDS, n_words);
+    const uint64_t offs[8] = {sec.freq, sec.scales, sec.dir, sec.states,
+                              sec.words, sec.esc_idx, sec.esc_val, sec.total};
+    for (int i = 0; i < 8; ++i) wr64(b + H_OFF_FREQ + 8 * i, offs[i]);
+
+    auto zero_to = [&](uint64_t from, uint64_t to) {
+        if (to > from) std::memset(b + from, 0, to - from);
+    };
+    zero_to(sec.freq, sec.total);  // gaps and padding words are zero
+    for (int s = 0; s < 256; ++s) wr16(b + sec.freq + 2 * s, t->freq[s]);
+    std::memcpy(b + sec.scales, scales, d->rows * 4);
+
+    std::vector<uint64_t> first(n_chunks);
+    for (uint64_t k = 0, at = 0; k < n_chunks; ++k) {
+        first[k] = at;
+        at += round_up(wcount[k], kWordPad);
+        wr64(b + sec.dir + kDirEntryBytes * k, first[k]);
+        wr32(b + sec.dir + kDirEntryBytes * k + 8, (uint32_t)wcount[k]);
+    }
+    std::memcpy(b + sec.states, states.get(), n_chunks * kLanes * 4);
+    parallel_for(n_chunks, [&](uint64_t k) {
+        const uint64_t p0 = k * Z;
+        const uint64_t nk = std::min<uint64_t>(Z, n - p0);
+        const uint16_t *src = scratch.get() + p0 + nk - wcount[k];
+        std::memcpy(b + sec.words + 2 * first[k], src, 2 * wcount[k]);
+    });
+    for (uint64_t e = 0; e < n_esc; ++e) {
+        wr64(b + sec.esc_idx + 8 * e, esc_idx[e]);
+        wr16(b + sec.esc_val + 2 * e, esc_bf16[e]);
+    }
+    return EQ_OK;
+}
+
+eq_status eq_parse_header(const void *bytes, uint64_t len, eq_header *out) {
+    if (!bytes || !out) return EQ_EINVAL;
+    const uint8_t *b = static_cast<const uint8_t *>(bytes);
+    if (len < kHeaderBytes) return EQ_ECORRUPT;
+    if (rd32(b + H_MAGIC) != kMagic || rd16(b + H_VERSION) != kVersion) return EQ_ECORRUPT;
+    eq_header h{};
+    h.dtype = b[H_DTYPE];
+    h.flags = b[H_FLAGS];
+    h.rows = rd64(b + H_ROWS);
+    h.cols = rd64(b + H_COLS);
+    h.n = rd64(b + H_N);
+    h.chunk_symbols = rd32(b + H_CHUNK);
+    h.lane_run = rd32(b + H_LANE_RUN);
+    h.n_chunks = rd64(b + H_NCHUNKS);
+    h.n_esc = rd64(b + H_NESC);
+    h.esc_code = b[H_ESC_CODE];
+    h.n_words = rd64(b + H_NWORDS);
+    h.off_freq = rd64(b + H_OFF_FREQ);
+    h.off_scales = rd64(b + H_OFF_SCALES);
+    h.off_dir = rd64(b + H_OFF_DIR);
+    h.off_states = rd64(b + H_OFF_STATES);
+    h.off_words = rd64(b + H_OFF_WORDS);
+    h.off_esc_idx = rd64(b + H_OFF_ESC_IDX);
+    h.off_esc_val = rd64(b + H_OFF_ESC_VAL);
+    h.total_bytes = rd64(b + H_TOTAL);
+    h.single_symbol = -1;
+
+    if (h.dtype != EQ_DTYPE_INT8 && h.dtype != EQ_DTYPE_E4M3) return EQ_ECORRUPT;
+    if (h.flags > 1 || (!(h.flags & 1) && (h.n_esc || h.esc_code))) return EQ_ECORRUPT;
+    if (rd32(b + H_LANES) != kLanes || rd32(b + H_PROB_BITS) != kProbBits) return EQ_ECORRUPT;
+    if (!valid_lane_run(h.lane_run)) return EQ_ECORRUPT;
+    if (h.chunk_symbols == 0 || h.chunk_symbols > kMaxChunk ||
+        h.chunk_symbols % (kLanes * h.lane_run))
+        return EQ_ECORRUPT;
+    if (h.rows == 0 || h.cols == 0 || h.cols > (1ull << 40) / h.rows || h.rows * h.cols != h.n)
+        return EQ_ECORRUPT;
+    if (h.n_chunks != (h.n + h.chunk_symbols - 1) / h.chunk_symbols) return EQ_ECORRUPT;
+    if (h.n_esc > h.n || h.n_words > h.n + 8 * h.n_chunks) return EQ_ECORRUPT;
+    for (size_t i = 65; i < 72; ++i)
+        if (b[i]) return EQ_ECORRUPT;
+    for (size_t i = 144; i < kHeaderBytes; ++i)
+        if (b[i]) return EQ_ECORRUPT;
+    const Sections sec = layout(h.rows, h.n_chunks, h.n_words, h.n_esc);
+    if (h.off_freq != sec.freq || h.off_scales != sec.scales || h.off_dir != sec.dir ||
+        h.off_states != sec.states || h.off_words != sec.words || h.off_esc_idx != sec.esc_idx ||
+        h.off_esc_val != sec.esc_val || h.total_bytes != sec.total)
+        return EQ_ECORRUPT;
+    if (len < h.total_bytes) return EQ_ECORRUPT;
+
+    uint32_t fsum = 0;
+    for (int s = 0; s < 256; ++s) {
+        const uint16_t f = rd16(b + h.off_freq + 2 * s);
+        fsum += f;
+        if (f == kProbScale) h.single_symbol = s;
+    }
+    if (fsum != kProbScale) return EQ_ECORRUPT;
+
+    // directory: consecutive padded word ranges covering exactly n_words
+    uint64_t at = 0;
+    for (uint64_t k = 0; k < h.n_chunks; ++k) {
+        const uint8_t *e = b + h.off_dir + kDirEntryBytes * k;
+        const uint64_t first = rd64(e);
+        const uint32_t count = rd32(e + 8);
+        const uint64_t nk = std::min<uint64_t>(h.chunk_symbols, h.n - k * h.chunk_symbols);
+        if (first != at || count > nk || rd32(e + 12) != 0) return EQ_ECORRUPT;
+        at += round_up(count, kWordPad);
+    }
+    if (at != h.n_words) return EQ_ECORRUPT;
+    // lane states: a valid encoder end state lies in [2^16, 2^32)
+    for (uint64_t i = 0; i < h.n_chunks * kLanes; ++i)
+        if (rd32(b + h.off_states + 4 * i) < kStateLow) return EQ_ECORRUPT;
+    for (uint64_t e = 0; e < h.n_esc; ++e) {
+        const uint64_t idx = rd64(b + h.off_esc_idx + 8 * e);
+        if (idx >= h.n || (e && idx <= rd64(b + h.off_esc_idx + 8 * (e - 1)))) return EQ_ECORRUPT;
+    }
+    *out = h;
+    return EQ_OK;
+}
+
+}  // extern "C"

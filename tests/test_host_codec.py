@@ -1,0 +1,237 @@
+"""CPU checks of libeq's host side: the exported C ABI, eq_build_tables and
+eq_encode_host against the oracle (byte-equal containers), eq_parse_header
+validation and the encoder's argument checks. No GPU call is made here."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from rans_decode_amd import eq
+
+
+def test_library_exports_every_declared_function():
+    names = eq.declared_functions()
+    assert {"eq_build_tables", "eq_encode_host", "eq_decode_block", "eq_decode_dequant_bf16"} <= set(names)
+    lib = ctypes.CDLL(eq.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_struct_sizes_match_c_layout():
+    assert ctypes.sizeof(eq.eq_tables) == 3600
+    assert ctypes.sizeof(eq.eq_tensor_desc) == 40
+    assert ctypes.sizeof(eq.eq_header) == 136
+    assert ctypes.sizeof(eq.eq_tensor_ref) == 152
+    assert ctypes.sizeof(eq.eq_block) == 24
+
+
+def test_status_strings():
+    assert eq.status_string(0) == "ok"
+    assert "corrupt" in eq.status_string(-3)
+
+
+def _tables_equal_oracle(sym):
+    t = eq.build_tables(sym)
+    f = np.array(t.freq, dtype=np.uint16)
+    assert np.array_equal(f, oracle.build_freq(sym))
+    assert list(t.cum) == list(np.concatenate([[0], np.cumsum(f.astype(np.int64))]))
+    assert np.array_equal(np.array(t.counts, np.uint64), np.bincount(sym, minlength=256).astype(np.uint64))
+    return t
+
+
+def test_build_tables_matches_oracle_random():
+    rng = np.random.default_rng(3)
+    for it in range(400):
+        n = int(rng.integers(1, 5000))
+        k = int(rng.integers(1, 257))
+        present = rng.choice(256, size=k, replace=False)
+        w = rng.pareto(0.7, k) + 1e-4
+        sym = present[rng.choice(k, size=n, p=w / w.sum())].astype(np.uint8)
+        _tables_equal_oracle(sym)
+
+
+def test_build_tables_matches_oracle_quantiser_hand_cases():
+    from conftest import read_golden
+    for case in read_golden("quantizer_cases.txt")["case"]:
+        lhs = case.split("->")[0]
+        parts = []
+        for tok in lhs.split():
+            b, c = tok.split(":")
+            parts.append(np.full(int(c), int(b), np.uint8))
+        _tables_equal_oracle(np.concatenate(parts))
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_encode_byte_equal_to_oracle_configs(cfg):
+    spec = synth.config_specs(cfg)[0]
+    t = synth.make_tensor(cfg, 0, 0)
+    tab = _tables_equal_oracle(t.symbols)
+    ours = eq.encode_host(tab, spec.dtype, spec.rows, spec.cols, t.symbols, t.scales)
+    ref = oracle.encode(spec.dtype, spec.rows, spec.cols, t.symbols, t.scales,
+                        np.array(tab.freq, np.uint16))
+    assert ours.size == ref.size and np.array_equal(ours, ref)
+
+
+def test_encode_byte_equal_escapes_and_e4m3():
+    spec = synth.TensorSpec("down", 48, 4096, synth.DTYPE_INT8, 2.1, 4)
+    t = synth.make_tensor(4, 0, 6, spec=spec)
+    tab = eq.build_tables(t.symbols)
+    ours = eq.encode_host(tab, spec.dtype, spec.rows, spec.cols, t.symbols, t.scales,
+                          t.esc_idx, t.esc_val, esc_code=t.esc_code)
+    ref = oracle.encode(spec.dtype, spec.rows, spec.cols, t.symbols, t.scales,
+                        np.array(tab.freq, np.uint16), esc_enabled=True, esc_code=t.esc_code,
+                        esc_idx=t.esc_idx, esc_val=t.esc_val)
+    assert np.array_equal(ours, ref)
+    spec3 = synth.TensorSpec("q", 128, 4096, synth.DTYPE_E4M3, 2.1)
+    t3 = synth.make_tensor(3, 0, 0, spec=spec3)
+    tab3 = eq.build_tables(t3.symbols)
+    ours = eq.encode_host(tab3, spec3.dtype, spec3.rows, spec3.cols, t3.symbols, t3.scales)
+    ref = oracle.encode(spec3.dtype, spec3.rows, spec3.cols, t3.symbols, t3.scales,
+                        np.array(tab3.freq, np.uint16))
+    assert np.array_equal(ours, ref)
+
+
+def test_encode_byte_equal_random_layouts():
+    rng = np.random.default_rng(11)
+    for it in range(600):
+        K = int(rng.choice([1, 2, 4, 8, 16]))
+        Z = 64 * K * int(rng.integers(1, 6))
+        n = int(rng.integers(1, 4 * Z + 1))
+        k = int(rng.integers(1, 30))
+        present = rng.choice(256, size=k, replace=False)
+        w = rng.exponential(1.0, k) ** 2 + 1e-3
+        sym = present[rng.choice(k, size=n, p=w / w.sum())].astype(np.uint8)
+        divs = [d for d in range(1, n + 1) if n % d == 0]
+        rows = int(rng.choice(divs))
+        cols = n // rows
+        scales = rng.uniform(-1, 1, rows).astype(np.float32)
+        tab = eq.build_tables(sym)
+        ours = eq.encode_host(tab, 1, rows, cols, sym, scales, chunk_symbols=Z, lane_run=K)
+        ref = oracle.encode(1, rows, cols, sym, scales, np.array(tab.freq, np.uint16), Z, K)
+        assert np.array_equal(ours, ref), (it, K, Z, n)
+
+
+def test_encode_custom_table_byte_equal():
+    freq = np.zeros(256, np.uint16)
+    freq[[0, 1, 0xFF]] = [4000, 80, 16]
+    sym = np.array([0xFF, 0xFF, 1, 0], np.uint8)
+    ours = eq.encode_host(eq.tables_from_freq(freq), 1, 1, 4, sym, np.array([0.01], np.float32),
+                          chunk_symbols=512)
+    ref = oracle.encode(1, 1, 4, sym, np.array([0.01], np.float32), freq, 512, 8)
+    assert np.array_equal(ours, ref)
+
+
+def test_parse_header_matches_oracle_fields():
+    t = synth.make_tensor(1, 0, 0)
+    c = eq.encode_host(eq.build_tables(t.symbols), 1, 1024, 1024, t.symbols, t.scales)
+    h = eq.parse_header(c)
+    o = oracle.header(c)
+    for k in ("rows", "cols", "n", "n_chunks", "n_esc", "n_words", "off_freq", "off_scales",
+              "off_dir", "off_states", "off_words", "off_esc_idx", "off_esc_val"):
+        assert getattr(h, k) == o[k], k
+    assert h.total_bytes == o["total"] and h.chunk_symbols == 65536 and h.lane_run == 8
+    assert h.single_symbol == -1
+
+
+def test_parse_header_single_symbol():
+    sym = np.full(5000, 0x07, np.uint8)
+    c = eq.encode_host(eq.build_tables(sym), 1, 50, 100, sym, np.ones(50, np.float32))
+    assert eq.parse_header(c).single_symbol == 7
+
+
+def _corrupt_cases(c):
+    o = oracle.header(c)
+    cases = {}
+
+    def mod(name, fn):
+        x = c.copy()
+        fn(x)
+        cases[name] = x
+    mod("magic", lambda x: x.__setitem__(0, 0))
+    mod("version", lambda x: x.__setitem__(4, 2))
+    mod("dtype", lambda x: x.__setitem__(6, 9))
+    mod("lane_run", lambda x: x.__setitem__(36, 3))
+    mod("rows", lambda x: x.__setitem__(8, x[8] ^ 1))
+    mod("freq_sum", lambda x: x.__setitem__(o["off_freq"], x[o["off_freq"]] ^ 1))
+    mod("dir_start", lambda x: x.__setitem__(o["off_dir"] + 16, x[o["off_dir"] + 16] ^ 8))
+    mod("dir_count", lambda x: x.__setitem__(o["off_dir"] + 8 + 2, 0x7F))
+    mod("state_low", lambda x: x.__setitem__(slice(o["off_states"] + 2, o["off_states"] + 4), 0))
+    mod("offset", lambda x: x.__setitem__(96, x[96] ^ 0x80))
+    mod("header_pad", lambda x: x.__setitem__(200, 1))
+    cases["truncated"] = c[:-256].copy()
+    return cases
+
+
+def test_parse_header_rejects_corruption():
+    t = synth.make_tensor(1, 0, 0)
+    c = eq.encode_host(eq.build_tables(t.symbols), 1, 1024, 1024, t.symbols, t.scales)
+    eq.parse_header(c)
+    for name, bad in _corrupt_cases(c).items():
+        with pytest.raises(eq.EqError) as ei:
+            eq.parse_header(bad)
+        assert ei.value.status == eq.EQ_ECORRUPT, name
+
+
+def test_parse_header_rejects_unsorted_escapes():
+    spec = synth.TensorSpec("down", 16, 4096, synth.DTYPE_INT8, 2.1, 4)
+    t = synth.make_tensor(4, 0, 6, spec=spec)
+    c = eq.encode_host(eq.build_tables(t.symbols), 1, 16, 4096, t.symbols, t.scales, t.esc_idx,
+                       t.esc_val, esc_code=0x80)
+    h = eq.parse_header(c)
+    bad = c.copy()
+    a = h.off_esc_idx
+    bad[a:a + 8], bad[a + 8:a + 16] = c[a + 8:a + 16], c[a:a + 8]
+    with pytest.raises(eq.EqError):
+        eq.parse_header(bad)
+
+
+def test_encode_argument_errors():
+    sym = np.zeros(1024, np.uint8)
+    sym[5] = 3
+    tab = eq.build_tables(sym)
+    sc = np.ones(16, np.float32)
+    good = dict(dtype=1, rows=16, cols=64)
+
+    def enc(**kw):
+        a = dict(good)
+        a.update(kw)
+        return eq.encode_host(kw.pop("tab", tab), a["dtype"], a["rows"], a["cols"], kw.get("sym", sym),
+                              kw.get("sc", sc), kw.get("esc_idx"), kw.get("esc_val"),
+                              esc_code=kw.get("esc_code", 0), chunk_symbols=kw.get("Z", 512),
+                              lane_run=kw.get("K", 8))
+    enc()
+    bad_cases = [
+        dict(K=3), dict(Z=500), dict(Z=0), dict(dtype=7),
+        dict(sc=np.array([np.inf] + [1.0] * 15, np.float32)),
+        dict(sym=np.full(1024, 9, np.uint8)),                      # byte with frequency 0
+        dict(esc_code=3),                                           # escape code present, not listed
+        dict(esc_code=3, esc_idx=np.array([6], np.uint64), esc_val=np.array([1], np.uint16)),
+    ]
+    for kw in bad_cases:
+        with pytest.raises(eq.EqError) as ei:
+            enc(**kw)
+        assert ei.value.status == eq.EQ_EINVAL, kw
+    # E4M3 NaN code outside the escape list
+    s8 = np.zeros(1024, np.uint8)
+    s8[0] = 0x7F
+    with pytest.raises(eq.EqError):
+        eq.encode_host(eq.build_tables(s8), 2, 16, 64, s8, sc, chunk_symbols=512)
+    # empty input
+    with pytest.raises(eq.EqError):
+        eq.build_tables(np.zeros(0, np.uint8))
+
+
+def test_encode_size_query():
+    sym = np.zeros(4096, np.uint8)
+    sym[::3] = 1
+    tab = eq.build_tables(sym)
+    d = eq.eq_tensor_desc(dtype=1, lane_run=8, rows=64, cols=64, chunk_symbols=512)
+    need = ctypes.c_uint64(0)
+    sc = np.ones(64, np.float32)
+    st = eq._lib.eq_encode_host(ctypes.byref(tab), ctypes.byref(d), sym.ctypes.data, sc.ctypes.data,
+                                None, None, 0, None, 0, ctypes.byref(need))
+    assert st == eq.EQ_ERANGE
+    c = eq.eq_encode_host(tab, d, sym, sc)
+    assert c.size == need.value
