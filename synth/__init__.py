@@ -305,25 +305,34 @@ def _row_values_f64(spec: TensorSpec, sym_row: np.ndarray, scale: float) -> np.n
     return v * float(scale)
 
 
+def escapes_for(cfg: int, layer: int, t: int, spec: TensorSpec) -> tuple[np.ndarray, np.ndarray]:
+    """Super-weight side list (ascending flat indices, bf16 bits) of a tensor;
+    each value is +-100 x the std of its row's weights before substitution."""
+    if not spec.n_esc:
+        return np.zeros(0, np.uint64), np.zeros(0, np.uint16)
+    import torch  # bf16 rounding of the stored super-weight values (library routine)
+    pos, signs = _escape_positions(stream_key(cfg, layer, t, PURPOSE_ESCAPES), spec.n, spec.n_esc)
+    scales = scales_for(cfg, layer, t, spec.rows)
+    tab = table_for(spec)
+    key = stream_key(cfg, layer, t, PURPOSE_SYMBOLS)
+    vals = []
+    for p, sg in zip(pos, signs):
+        r = p // spec.cols
+        row = sample(tab, key, r * spec.cols, spec.cols)
+        std = float(np.std(_row_values_f64(spec, row, scales[r])))
+        v32 = torch.tensor([sg * 100.0 * std], dtype=torch.float32)
+        vals.append(int(v32.to(torch.bfloat16).view(torch.int16).item()) & 0xFFFF)
+    return np.array(pos, dtype=np.uint64), np.array(vals, dtype=np.uint16)
+
+
 def make_tensor(cfg: int, layer: int, t: int, spec: TensorSpec | None = None,
                 threads: int | None = None) -> Tensor:
     spec = spec or config_specs(cfg)[t]
     sym = sample(table_for(spec), stream_key(cfg, layer, t, PURPOSE_SYMBOLS), 0, spec.n, threads)
-    scales = scales_for(cfg, layer, t, spec.rows)
-    tensor = Tensor(spec, sym, scales)
+    tensor = Tensor(spec, sym, scales_for(cfg, layer, t, spec.rows))
     if spec.n_esc:
-        import torch  # bf16 rounding of the stored super-weight values (library routine)
-        pos, signs = _escape_positions(stream_key(cfg, layer, t, PURPOSE_ESCAPES), spec.n, spec.n_esc)
-        vals = []
-        for p, sg in zip(pos, signs):
-            r = p // spec.cols
-            row = sym[r * spec.cols:(r + 1) * spec.cols]
-            std = float(np.std(_row_values_f64(spec, row, scales[r])))
-            v32 = torch.tensor([sg * 100.0 * std], dtype=torch.float32)
-            vals.append(int(v32.to(torch.bfloat16).view(torch.int16).item()) & 0xFFFF)
-        sym[np.array(pos, dtype=np.int64)] = ESC_CODE[spec.dtype]
-        tensor.esc_idx = np.array(pos, dtype=np.uint64)
-        tensor.esc_val = np.array(vals, dtype=np.uint16)
+        tensor.esc_idx, tensor.esc_val = escapes_for(cfg, layer, t, spec)
+        sym[tensor.esc_idx.astype(np.int64)] = ESC_CODE[spec.dtype]
     return tensor
 
 
