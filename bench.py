@@ -74,7 +74,7 @@ def traffic_record(kernel_src: str):
         return None
 
 
-def build_block(cfg: int, layer: int = 0):
+def build_block(cfg: int, layer: int = 0, lane_run: int = 8):
     """Encode one block with the library's host encoder and place its
     containers in device memory. With EQ_BENCH_CACHE=<dir> the encoded
     containers are kept there as .npy files and reused."""
@@ -85,7 +85,7 @@ def build_block(cfg: int, layer: int = 0):
     cache = os.environ.get("EQ_BENCH_CACHE")
     conts = []
     for i, sp in enumerate(specs):
-        path = os.path.join(cache, f"cfg{cfg}_layer{layer}_t{i}.npy") if cache else None
+        path = os.path.join(cache, f"cfg{cfg}_layer{layer}_t{i}_k{lane_run}.npy") if cache else None
         if path and os.path.exists(path):
             blob = np.load(path)
         else:
@@ -95,7 +95,7 @@ def build_block(cfg: int, layer: int = 0):
             blob = eq.encode_host(tab, sp.dtype, sp.rows, sp.cols, t.symbols, t.scales,
                                   t.esc_idx if esc else None, t.esc_val if esc else None,
                                   esc_code=t.esc_code if esc else 0,
-                                  chunk_symbols=synth.CHUNK_SYMBOLS, lane_run=synth.LANE_RUN)
+                                  chunk_symbols=synth.CHUNK_SYMBOLS, lane_run=lane_run)
             del t
             if path:
                 os.makedirs(cache, exist_ok=True)
@@ -191,7 +191,7 @@ def bench_block(args):
     from rans_decode_amd import eq
 
     t0 = time.perf_counter()
-    specs, conts = build_block(4)
+    specs, conts = build_block(4, 0, args.lane_run)
     offs = synth.block_offsets(specs)
     n = offs[-1]
     log(f"block built in {time.perf_counter() - t0:.1f} s: {n} weights, "
@@ -246,7 +246,7 @@ def bench_block(args):
         "config": {
             "workload": "70B-shaped block decode+dequant: q,o 8192x8192; k,v 1024x8192; "
                         "gate,up 28672x8192; down 8192x28672; int8 2.1-bit Laplace codes, "
-                        "64Ki-symbol chunks, 64 lanes, K=8, 4 super-weight escapes, bf16 out",
+                        f"64Ki-symbol chunks, 64 lanes, K={args.lane_run}, 4 super-weight escapes, bf16 out",
             "weights": n,
             "container_bytes": total_container,
             "effective_bits_per_weight": round(8.0 * total_container / n, 4),
@@ -282,6 +282,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-ceiling", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--lane-run", type=int, default=8, choices=[1, 2, 4, 8, 16],
+                    help="container lane run K of the encoded block (workload parameter)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this decoder has no multi-GPU path "

@@ -24,17 +24,20 @@ def _run(cmd, verbose):
     subprocess.check_call(cmd, cwd=ROOT)
 
 
-def build_library(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    host_o = os.path.join(BUILD, "host_codec.o")
-    dev_o = os.path.join(BUILD, "decode.o")
+def build_library(verbose: bool = False, out: str = LIB, defines: dict | None = None,
+                  build_dir: str = BUILD) -> str:
+    """Build libeq.so (or a variant with extra -D defines at `out`)."""
+    os.makedirs(build_dir, exist_ok=True)
+    host_o = os.path.join(build_dir, "host_codec.o")
+    dev_o = os.path.join(build_dir, "decode.o")
+    dflags = [f"-D{k}={v}" for k, v in (defines or {}).items()]
     _run(["g++", "-O2", "-std=c++17", "-fPIC", "-pthread", "-Wall", "-Wextra",
           "-c", os.path.join(CSRC, "host_codec.cpp"), "-o", host_o], verbose)
-    _run(["hipcc", *HIPCC_FLAGS, "-c", os.path.join(CSRC, "decode.hip"), "-o", dev_o], verbose)
-    tmp = LIB + ".tmp"
+    _run(["hipcc", *HIPCC_FLAGS, *dflags, "-c", os.path.join(CSRC, "decode.hip"), "-o", dev_o], verbose)
+    tmp = out + ".tmp"
     _run(["hipcc", "-shared", f"--offload-arch={ARCH}", host_o, dev_o, "-o", tmp, "-pthread"], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -35,23 +35,42 @@
 
 namespace {
 
-constexpr int kWaves = 8;                  // chunks (waves) per workgroup
+// Tunables (compile-time): chunks (waves) per workgroup and the per-wave
+// ring of renormalisation words in LDS.
+#ifndef EQ_WAVES
+#define EQ_WAVES 8
+#endif
+#ifndef EQ_RING_WORDS
+#define EQ_RING_WORDS 1024
+#endif
+#ifndef EQ_RENORM_BRANCHLESS
+#define EQ_RENORM_BRANCHLESS 1
+#endif
+#ifndef EQ_LUT8
+#define EQ_LUT8 1
+#endif
+constexpr int kWaves = EQ_WAVES;
 constexpr int kThreads = 64 * kWaves;
-constexpr uint32_t kRing = 1024;           // renormalisation-word ring per wave (power of 2)
-constexpr uint32_t kRingAlloc = kRing + 64;  // + copy of the ring's first 64 words
-constexpr uint32_t kBlk = 512;             // words per ring refill: 16 bytes per lane
+constexpr uint32_t kRing = EQ_RING_WORDS;       // power of two
+constexpr uint32_t kBlk = kRing / 2;            // words per refill
+constexpr uint32_t kLaneWords = kBlk / 64;      // words each lane loads per refill
+constexpr uint32_t kCheck = kBlk / 64;          // steps between refill checks
+constexpr uint32_t kRingAlloc = kRing + 64;     // + copy of the ring's first 64 words
+static_assert(kRing == 1024 || kRing == 512, "ring of 512 or 1024 words");
 
+// Output modes of a tensor (host-chosen).
 enum : uint32_t {
-    F_FAST = 1u,   // aligned vector stores + (bf16) at most two rows per 64K group
-    F_CONST = 2u,  // one-symbol tensor (frequency 4096): nothing to decode
+    M_GENERAL = 0,  // any shape / alignment: per-element scale and stores
+    M_ROW1 = 1,     // every 64K group lies in one row (bf16), or aligned u8 stores
+    M_ROW2 = 2,     // a 64K group spans at most two rows (bf16)
 };
 
 struct TArgs {
     const uint8_t *base;  // container (device)
     uint64_t out_offset, n, cols, rows, n_chunks, n_words, n_esc;
     uint64_t off_scales, off_dir, off_states, off_words, off_esc_idx, off_esc_val, off_freq;
-    uint32_t Z, dtype, flags, const_sym;
-    uint32_t wg_begin, pad;
+    uint32_t Z, dtype, mode, const_sym;
+    uint32_t is_const, wg_begin;
 };
 
 struct LArgs {
@@ -71,15 +90,41 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
 
-// Value of the symbol byte held in bits 0..7 of a slot-table entry.
+#if EQ_LUT8
+// 8-byte slot-table entry: lo = f | symbol << 24 (bits 12..23 zero, so a
+// 24-bit multiply sees f alone), hi = slot - cum.
+typedef uint2 LutEnt;
+constexpr int kSymShift = 24;
+__device__ __forceinline__ uint32_t ent_bits(LutEnt e) { return e.x; }
+__device__ __forceinline__ LutEnt make_ent(uint32_t s, uint32_t f, uint32_t bias) {
+    return make_uint2(f | (s << 24), bias);
+}
+__device__ __forceinline__ uint32_t ent_next(LutEnt e, uint32_t x) {
+    return __umul24(e.x, x >> 12) + e.y;
+}
+#else
+// 4-byte slot-table entry: symbol | f << 8 | (slot - cum) << 20.
+typedef uint32_t LutEnt;
+constexpr int kSymShift = 0;
+__device__ __forceinline__ uint32_t ent_bits(LutEnt e) { return e; }
+__device__ __forceinline__ LutEnt make_ent(uint32_t s, uint32_t f, uint32_t bias) {
+    return s | (f << 8) | (bias << 20);
+}
+__device__ __forceinline__ uint32_t ent_next(LutEnt e, uint32_t x) {
+    return __umul24((e >> 8) & 0xFFFu, x >> 12) + (e >> 20);
+}
+#endif
+
+// Value of the symbol byte held in a slot-table entry's bits kSymShift..+8.
 template <uint32_t DT>
-__device__ __forceinline__ float sym_value(uint32_t ent) {
+__device__ __forceinline__ float sym_value(uint32_t bits) {
     if constexpr (DT == EQ_DTYPE_INT8) {
-        return (float)(int32_t)(int8_t)(ent & 0xFFu);
+        return (float)(int32_t)(int8_t)((bits >> kSymShift) & 0xFFu);
     } else {
-        return __builtin_amdgcn_cvt_f32_fp8((int)ent, 0);  // OCP E4M3FN on gfx950
+        return __builtin_amdgcn_cvt_f32_fp8((int)bits, kSymShift / 8);  // OCP E4M3FN on gfx950
     }
 }
+__device__ __forceinline__ uint32_t sym_byte(uint32_t bits) { return (bits >> kSymShift) & 0xFFu; }
 
 __device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
 
@@ -90,7 +135,7 @@ __device__ __forceinline__ void raise_flag(uint32_t *status, uint32_t bits, uint
 // Slot table of the tensor: for every slot in [0, 4096) the byte s with
 // cum[s] <= slot < cum[s] + f[s], packed as s | f << 8 | (slot - cum[s]) << 20
 // (f <= 4095 here; a one-symbol tensor never builds a table).
-__device__ void build_lut(const TArgs &T, uint32_t *lut, uint32_t *cum) {
+__device__ void build_lut(const TArgs &T, LutEnt *lut, uint32_t *cum) {
     const uint16_t *freq = reinterpret_cast<const uint16_t *>(T.base + T.off_freq);
     const uint32_t tid = threadIdx.x;
     if (tid < 64) {
@@ -124,50 +169,76 @@ __device__ void build_lut(const TArgs &T, uint32_t *lut, uint32_t *cum) {
             if (cum[mid] <= slot) lo = mid; else hi = mid;
         }
         const uint32_t f = cum[lo + 1] - cum[lo];
-        lut[slot] = lo | (f << 8) | ((slot - cum[lo]) << 20);
+        lut[slot] = make_ent(lo, f, slot - cum[lo]);
     }
     __syncthreads();
 }
 
-__device__ __forceinline__ uint4 load_block(const uint16_t *words, uint32_t b, uint32_t wpad,
-                                            uint32_t lane) {
-    const uint32_t w0 = b * kBlk + lane * 8u;
-    uint4 v = {0u, 0u, 0u, 0u};
-    if (w0 < wpad) v = *reinterpret_cast<const uint4 *>(words + w0);
+template <uint32_t LW> struct LaneBlock;
+template <> struct LaneBlock<8> { using type = uint4; };
+template <> struct LaneBlock<4> { using type = uint2; };
+using Blk = LaneBlock<kLaneWords>::type;
+
+__device__ __forceinline__ Blk load_block(const uint16_t *words, uint32_t b, uint32_t wpad,
+                                          uint32_t lane) {
+    const uint32_t w0 = b * kBlk + lane * kLaneWords;
+    Blk v{};
+    if (w0 < wpad) v = *reinterpret_cast<const Blk *>(words + w0);
     return v;
 }
 
-// Block b lands at ring position (b * 512) mod R; the block written at 0 is
+// Block b lands at ring position (b * kBlk) mod R; the block written at 0 is
 // also copied to [R, R + 64) so that a read at (ptr mod R) + rank, rank < 64,
 // never has to wrap.
-__device__ __forceinline__ void put_block(uint16_t *ring, uint32_t b, uint4 v, uint32_t lane) {
+__device__ __forceinline__ void put_block(uint16_t *ring, uint32_t b, Blk v, uint32_t lane) {
     const uint32_t pos = (b * kBlk) & (kRing - 1u);
-    *reinterpret_cast<uint4 *>(ring + pos + lane * 8u) = v;
-    if (pos == 0 && lane < 8u) *reinterpret_cast<uint4 *>(ring + kRing + lane * 8u) = v;
+    *reinterpret_cast<Blk *>(ring + pos + lane * kLaneWords) = v;
+    if (pos == 0 && lane < 64u / kLaneWords)
+        *reinterpret_cast<Blk *>(ring + kRing + lane * kLaneWords) = v;
 }
 
-// Per-chunk decoder state of one wave.
-template <int K, bool BF16, uint32_t DT, bool FAST>
+// Per-chunk decoder state of one wave. Positions inside the chunk are u32
+// (a chunk holds at most 2^24 symbols); wave-uniform values stay in SGPRs.
+template <int K, bool BF16, uint32_t DT, int MODE>
 struct Chunk {
     const TArgs &T;
-    const uint32_t *lut;
+    const LutEnt *lut;
     uint16_t *ring;
     uint32_t lane;
     uint64_t p0;   // flat position of the chunk's first symbol
     uint32_t nk;   // symbols in the chunk
     uint32_t wc, wpad, nblocks, nb;
     const uint16_t *words;
-    uint4 pend;
+    Blk pend;
     uint32_t x;    // this lane's rANS state
     uint32_t ptr;  // words consumed (wave-uniform)
-    uint64_t row_base, col_base;  // row / column of the current group's first symbol
-    float s_cur, s_next;          // scales of rows row_base and row_base + 1
-    uint64_t esc_i, esc_pos;
+    uint64_t row;  // row of the current group's first symbol (modes 1, 2)
+    uint32_t col;  // its column
+    float s_cur, s_next;  // scales of rows row and row + 1
+    uint64_t esc_i;       // index of the next super weight in the side list
+    uint32_t esc_loc;     // its chunk-local position, ~0u if none left in the chunk
+    // tensor fields used inside the loop, read once per chunk
+    uint64_t cols, rows, n_esc;
+    uint32_t cols32;
+    const float *scales;
+    const uint64_t *eidx;
+    const uint16_t *eval;
+    char *ob;             // output of the chunk's first symbol
 
     static constexpr uint32_t G = 64u * K;  // symbols per group of K steps
 
-    // Keep at least 512 staged words ahead of ptr (one group of K <= 8 steps,
-    // or half of a K = 16 group, reads at most 512 words).
+    __device__ __forceinline__ const uint64_t *esc_idx() const { return eidx; }
+    __device__ __forceinline__ const uint16_t *esc_val() const { return eval; }
+    __device__ __forceinline__ void load_esc() {
+        esc_loc = ~0u;
+        if (esc_i < n_esc) {
+            const uint64_t e = esc_idx()[esc_i];
+            if (e < p0 + nk) esc_loc = (uint32_t)(e - p0);
+        }
+    }
+
+    // Keep at least kBlk staged words ahead of ptr: kCheck steps read at most
+    // 64 * kCheck = kBlk words.
     __device__ __forceinline__ void refill() {
         if (nb < nblocks && (int32_t)(nb * kBlk - ptr) < (int32_t)kBlk) {
             put_block(ring, nb, pend, lane);
@@ -180,40 +251,58 @@ struct Chunk {
     // >= 2^16, so they never ask for a word).
     template <bool MASKED>
     __device__ __forceinline__ uint32_t step(bool active) {
-        const uint32_t ent = lut[x & 4095u];
-        uint32_t xn = __umul24((ent >> 8) & 0xFFFu, x >> 12) + (ent >> 20);
+        const LutEnt ent = lut[x & 4095u];
+        uint32_t xn = ent_next(ent, x);
         if (MASKED) xn = active ? xn : x;
         const bool need = xn < 65536u;
         const uint64_t m = __builtin_amdgcn_ballot_w64(need);
-        if (need) {
-            const uint32_t rank = __builtin_amdgcn_mbcnt_hi(
-                (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-            xn = (xn << 16) | ring[(ptr & (kRing - 1u)) + rank];
-        }
+        const uint32_t rank = __builtin_amdgcn_mbcnt_hi(
+            (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+#if EQ_RENORM_BRANCHLESS
+        // every lane reads ring[ptr + rank] (always inside the staged window
+        // plus its 64-word copy); only lanes that need a word keep it
+        const uint32_t w = ring[(ptr & (kRing - 1u)) + rank];
+        const uint32_t merged = (xn << 16) | w;
+        uint32_t sel;
+        // a VALU select on the ballot mask (keeps the ring read unconditional)
+        asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(sel) : "v"(xn), "v"(merged), "s"(m));
+        xn = sel;
+#else
+        if (need) xn = (xn << 16) | ring[(ptr & (kRing - 1u)) + rank];
+#endif
         ptr += (uint32_t)__builtin_popcountll(m);
         x = xn;
-        return ent;
+        return ent_bits(ent);
     }
 
-    // The K outputs of this lane for group g, then patches and store.
+    __device__ __forceinline__ float row_scale(uint64_t r) const {
+        typedef const float __attribute__((address_space(4))) cfloat;
+        cfloat *sc = (cfloat *)scales;
+        return sc[r < rows ? r : rows - 1];
+    }
+
+    // The K outputs of this lane for group g, super-weight patches, store.
     template <bool MASKED>
     __device__ __forceinline__ void group(uint32_t g, void *out) {
-        const uint32_t q0 = g * G + lane * (uint32_t)K;  // chunk-local first position
+        const uint32_t g0 = g * G;                        // chunk-local group start
+        const uint32_t q0 = g0 + lane * (uint32_t)K;      // this lane's first position
         uint32_t ent[K];
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            if ((k & 7) == 0) refill();
+            if ((k & (kCheck - 1)) == 0) refill();
             ent[k] = step<MASKED>(q0 + (uint32_t)k < nk);
         }
-        const uint64_t g0 = p0 + (uint64_t)g * G;  // flat position of the group
         if constexpr (BF16) {
-            uint16_t *ob = static_cast<uint16_t *>(out) + T.out_offset;
-            if constexpr (FAST) {
+            uint16_t *ob = reinterpret_cast<uint16_t *>(this->ob);
+            if constexpr (MODE != M_GENERAL) {
                 if (!MASKED) {
-                    // lanes below b are in row_base, the others in row_base + 1
-                    const uint64_t b64 = (T.cols - col_base) / (uint32_t)K;
-                    const uint32_t b = b64 < 64u ? (uint32_t)b64 : 64u;
-                    const float s = lane < b ? s_cur : s_next;
+                    float s = s_cur;
+                    if constexpr (MODE == M_ROW2) {
+                        // lanes below b are in `row`, the others in row + 1
+                        const uint32_t left = (cols32 - col) / (uint32_t)K;
+                        const uint32_t b = left < 64u ? left : 64u;
+                        s = lane < b ? s_cur : s_next;
+                    }
                     uint32_t pk[(K + 1) / 2];
 #pragma unroll
                     for (int k = 0; k < K; k += 2) {
@@ -221,76 +310,68 @@ struct Chunk {
                         const float v1 = (k + 1 < K) ? sym_value<DT>(ent[k + 1]) * s : 0.0f;
                         pk[k / 2] = pack_bf16(v0, v1);
                     }
-                    patch_packed(g0, pk);
-                    store_packed(ob + g0 + lane * (uint32_t)K, pk);
+                    if (esc_loc < g0 + G) patch_packed(g0, pk);
+                    uint16_t *gb = ob + g0;  // wave-uniform base of the group
+                    store_packed(reinterpret_cast<char *>(gb) + lane * (2u * K), pk);
                     advance_row();
                     return;
                 }
             }
             // general path: any shape, partial groups, unaligned output
-            const float *sc = reinterpret_cast<const float *>(T.base + T.off_scales);
-            const uint64_t *eidx = reinterpret_cast<const uint64_t *>(T.base + T.off_esc_idx);
-            const uint16_t *eval = reinterpret_cast<const uint16_t *>(T.base + T.off_esc_val);
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 if (q0 + (uint32_t)k < nk) {
                     const uint64_t pos = p0 + q0 + (uint32_t)k;
-                    const float v = sym_value<DT>(ent[k]) * sc[pos / T.cols];
-                    uint16_t h = (uint16_t)(pack_bf16(v, 0.0f) & 0xFFFFu);
-                    ob[pos] = h;
+                    const float v = sym_value<DT>(ent[k]) * scales[pos / cols];
+                    ob[q0 + k] = (uint16_t)(pack_bf16(v, 0.0f) & 0xFFFFu);
                 }
             }
-            // super weights of this group (never past the chunk's end): the
-            // owning lane rewrites them after its own store of that element
-            const uint64_t lim = (g0 + G < p0 + nk) ? g0 + G : p0 + nk;
-            while (esc_pos < lim) {
-                const uint32_t off = (uint32_t)(esc_pos - g0);
-                if (lane == off / (uint32_t)K) ob[esc_pos] = eval[esc_i];
+            // super weights of this group: the owning lane rewrites them after
+            // its own store of that element (same thread, same address)
+            while (esc_loc < g0 + G) {
+                if (lane == (esc_loc - g0) / (uint32_t)K) ob[esc_loc] = esc_val()[esc_i];
                 ++esc_i;
-                esc_pos = esc_i < T.n_esc ? eidx[esc_i] : ~0ull;
+                load_esc();
             }
-            if constexpr (FAST) advance_row();
+            if constexpr (MODE != M_GENERAL) advance_row();
         } else {
-            uint8_t *ob = static_cast<uint8_t *>(out) + T.out_offset;
-            if (FAST && !MASKED) {
-                store_bytes(ob + g0 + lane * (uint32_t)K, ent);
+            uint8_t *ob = reinterpret_cast<uint8_t *>(this->ob);
+            if (MODE != M_GENERAL && !MASKED) {
+                store_bytes(reinterpret_cast<char *>(ob + g0) + lane * (uint32_t)K, ent);
             } else {
 #pragma unroll
                 for (int k = 0; k < K; ++k)
-                    if (q0 + (uint32_t)k < nk) ob[p0 + q0 + (uint32_t)k] = (uint8_t)ent[k];
+                    if (q0 + (uint32_t)k < nk) ob[q0 + k] = (uint8_t)sym_byte(ent[k]);
             }
         }
     }
 
-    // Scales of rows row_base and row_base + 1 (the last row repeats),
-    // read through the constant address space so they are scalar loads; they
-    // change only when a group crosses into the next row.
-    __device__ __forceinline__ float row_scale(uint64_t r) const {
-        typedef const float __attribute__((address_space(4))) cfloat;
-        cfloat *sc = (cfloat *)(T.base + T.off_scales);
-        return sc[r < T.rows ? r : T.rows - 1];
-    }
-
     __device__ __forceinline__ void advance_row() {
-        col_base += G;
-        if (col_base >= T.cols) {
-            col_base -= T.cols;
-            ++row_base;
-            s_cur = s_next;
-            s_next = row_scale(row_base + 1);
+        if constexpr (BF16 && MODE == M_ROW1) {
+            col += G;
+            if (col == cols32) {
+                col = 0;
+                ++row;
+                s_cur = row_scale(row);
+            }
+        } else if constexpr (BF16 && MODE == M_ROW2) {
+            col += G;
+            if (col >= cols32) {
+                col -= cols32;
+                ++row;
+                s_cur = s_next;
+                s_next = row_scale(row + 1);
+            }
         }
     }
 
-    // Super weights inside this group (FAST path: fix the packed registers of
-    // the owning lane before the store).
-    __device__ __forceinline__ void patch_packed(uint64_t g0, uint32_t *pk) {
-        if (esc_pos >= g0 + G) return;
-        const uint64_t *eidx = reinterpret_cast<const uint64_t *>(T.base + T.off_esc_idx);
-        const uint16_t *eval = reinterpret_cast<const uint16_t *>(T.base + T.off_esc_val);
+    // Super weights inside group g0 (fast paths): fix the owning lane's
+    // packed registers before the store.
+    __device__ __forceinline__ void patch_packed(uint32_t g0, uint32_t *pk) {
         do {
-            const uint32_t off = (uint32_t)(esc_pos - g0);
+            const uint32_t off = esc_loc - g0;
             const uint32_t owner = off / (uint32_t)K, e = off % (uint32_t)K;
-            const uint32_t v = eval[esc_i];
+            const uint32_t v = esc_val()[esc_i];
             if (lane == owner) {
 #pragma unroll
                 for (int i = 0; i < (K + 1) / 2; ++i) {
@@ -299,13 +380,13 @@ struct Chunk {
                 }
             }
             ++esc_i;
-            esc_pos = esc_i < T.n_esc ? eidx[esc_i] : ~0ull;
-        } while (esc_pos < g0 + G);
+            load_esc();
+        } while (esc_loc < g0 + G);
     }
 
-    __device__ __forceinline__ void store_packed(uint16_t *dst, const uint32_t *pk) {
+    __device__ __forceinline__ void store_packed(char *dst, const uint32_t *pk) {
         if constexpr (K == 1) {
-            *dst = (uint16_t)pk[0];
+            *reinterpret_cast<uint16_t *>(dst) = (uint16_t)pk[0];
         } else if constexpr (K == 2) {
             *reinterpret_cast<uint32_t *>(dst) = pk[0];
         } else if constexpr (K == 4) {
@@ -318,17 +399,17 @@ struct Chunk {
         }
     }
 
-    __device__ __forceinline__ void store_bytes(uint8_t *dst, const uint32_t *ent) {
+    __device__ __forceinline__ void store_bytes(char *dst, const uint32_t *ent) {
         if constexpr (K == 1) {
-            *dst = (uint8_t)ent[0];
+            *reinterpret_cast<uint8_t *>(dst) = (uint8_t)sym_byte(ent[0]);
         } else if constexpr (K == 2) {
-            *reinterpret_cast<uint16_t *>(dst) = (uint16_t)((ent[0] & 0xFFu) | ((ent[1] & 0xFFu) << 8));
+            *reinterpret_cast<uint16_t *>(dst) = (uint16_t)(sym_byte(ent[0]) | (sym_byte(ent[1]) << 8));
         } else {
             uint32_t w[K / 4];
 #pragma unroll
             for (int i = 0; i < K / 4; ++i)
-                w[i] = (ent[4 * i] & 0xFFu) | ((ent[4 * i + 1] & 0xFFu) << 8) |
-                       ((ent[4 * i + 2] & 0xFFu) << 16) | ((ent[4 * i + 3] & 0xFFu) << 24);
+                w[i] = sym_byte(ent[4 * i]) | (sym_byte(ent[4 * i + 1]) << 8) |
+                       (sym_byte(ent[4 * i + 2]) << 16) | (sym_byte(ent[4 * i + 3]) << 24);
             if constexpr (K == 4) {
                 *reinterpret_cast<uint32_t *>(dst) = w[0];
             } else if constexpr (K == 8) {
@@ -353,30 +434,37 @@ struct Chunk {
         nblocks = (wpad + kBlk - 1u) / kBlk;
         nb = 0;
         ptr = 0;
-        pend = make_uint4(0u, 0u, 0u, 0u);
+        pend = Blk{};
         if (nblocks) {
             put_block(ring, 0, load_block(words, 0, wpad, lane), lane);
             nb = 1;
             if (nb < nblocks) pend = load_block(words, nb, wpad, lane);
         }
-        row_base = p0 / T.cols;
-        col_base = p0 - row_base * T.cols;
-        if constexpr (BF16 && FAST) {
-            s_cur = row_scale(row_base);
-            s_next = row_scale(row_base + 1);
+        cols = T.cols;
+        cols32 = (uint32_t)T.cols;
+        rows = T.rows;
+        n_esc = T.n_esc;
+        scales = reinterpret_cast<const float *>(T.base + T.off_scales);
+        eidx = reinterpret_cast<const uint64_t *>(T.base + T.off_esc_idx);
+        eval = reinterpret_cast<const uint16_t *>(T.base + T.off_esc_val);
+        ob = static_cast<char *>(out) + (T.out_offset + p0) * (BF16 ? 2u : 1u);
+        if constexpr (BF16 && MODE != M_GENERAL) {
+            row = p0 / cols;
+            col = (uint32_t)(p0 - row * cols);
+            s_cur = row_scale(row);
+            s_next = row_scale(row + 1);
         }
-        esc_pos = ~0ull;
         esc_i = 0;
-        if (BF16 && T.n_esc) {
+        esc_loc = ~0u;
+        if (BF16 && n_esc) {
             // first super weight at or after p0
-            const uint64_t *eidx = reinterpret_cast<const uint64_t *>(T.base + T.off_esc_idx);
-            uint64_t lo = 0, hi = T.n_esc;
+            uint64_t lo = 0, hi = n_esc;
             while (lo < hi) {
                 const uint64_t mid = (lo + hi) >> 1;
-                if (eidx[mid] < p0) lo = mid + 1; else hi = mid;
+                if (esc_idx()[mid] < p0) lo = mid + 1; else hi = mid;
             }
             esc_i = lo;
-            esc_pos = lo < T.n_esc ? eidx[lo] : ~0ull;
+            load_esc();
         }
         // settle the set-up loads here rather than at the loop header, where
         // the wait would be repeated every group
@@ -410,8 +498,9 @@ __device__ void const_chunk(const TArgs &T, uint64_t chunk, uint32_t lane, void 
     for (uint32_t q = lane; q < nk; q += 64u) {
         const uint64_t pos = p0 + q;
         if constexpr (BF16) {
-            const float v = (T.dtype == EQ_DTYPE_INT8 ? sym_value<EQ_DTYPE_INT8>(T.const_sym)
-                                                       : sym_value<EQ_DTYPE_E4M3>(T.const_sym)) *
+            const uint32_t bits = T.const_sym << kSymShift;
+            const float v = (T.dtype == EQ_DTYPE_INT8 ? sym_value<EQ_DTYPE_INT8>(bits)
+                                                       : sym_value<EQ_DTYPE_E4M3>(bits)) *
                             sc[pos / T.cols];
             static_cast<uint16_t *>(out)[T.out_offset + pos] = (uint16_t)(pack_bf16(v, 0.0f) & 0xFFFFu);
         } else {
@@ -434,7 +523,7 @@ __device__ void const_chunk(const TArgs &T, uint64_t chunk, uint32_t lane, void 
 
 template <int K, bool BF16>
 __global__ void __launch_bounds__(kThreads) k_decode(LArgs a) {
-    __shared__ uint32_t lut[4096];
+    __shared__ LutEnt lut[4096];
     __shared__ __attribute__((aligned(16))) uint16_t rings[kWaves][kRingAlloc];
     __shared__ uint32_t cum[260];
 
@@ -445,7 +534,7 @@ __global__ void __launch_bounds__(kThreads) k_decode(LArgs a) {
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t lane = threadIdx.x & 63u;
     const uint64_t chunk = (uint64_t)(wg - T.wg_begin) * kWaves + wave;
-    const bool is_const = (T.flags & F_CONST) != 0;
+    const bool is_const = T.is_const != 0;
     if (!is_const) build_lut(T, lut, cum);
     if (chunk >= T.n_chunks) return;
     if (is_const) {
@@ -454,20 +543,23 @@ __global__ void __launch_bounds__(kThreads) k_decode(LArgs a) {
     }
     const uint64_t p0 = chunk * T.Z;
     const uint32_t nk = (uint32_t)umin64(T.Z, T.n - p0);
-    const bool fast = (T.flags & F_FAST) != 0;
-#define EQ_RUN(BF, DT, FA)                                                             \
+#define EQ_RUN(BF, DT, MO)                                                             \
     do {                                                                               \
-        Chunk<K, BF, DT, FA> c{T, lut, rings[wave], lane, p0, nk};                     \
+        Chunk<K, BF, DT, MO> c{T, lut, rings[wave], lane, p0, nk};                     \
         c.run(chunk, a.out, a.status);                                                 \
     } while (0)
     if constexpr (BF16) {
         if (T.dtype == EQ_DTYPE_INT8) {
-            if (fast) EQ_RUN(true, EQ_DTYPE_INT8, true); else EQ_RUN(true, EQ_DTYPE_INT8, false);
+            if (T.mode == M_ROW1) EQ_RUN(true, EQ_DTYPE_INT8, M_ROW1);
+            else if (T.mode == M_ROW2) EQ_RUN(true, EQ_DTYPE_INT8, M_ROW2);
+            else EQ_RUN(true, EQ_DTYPE_INT8, M_GENERAL);
         } else {
-            if (fast) EQ_RUN(true, EQ_DTYPE_E4M3, true); else EQ_RUN(true, EQ_DTYPE_E4M3, false);
+            if (T.mode == M_ROW1) EQ_RUN(true, EQ_DTYPE_E4M3, M_ROW1);
+            else if (T.mode == M_ROW2) EQ_RUN(true, EQ_DTYPE_E4M3, M_ROW2);
+            else EQ_RUN(true, EQ_DTYPE_E4M3, M_GENERAL);
         }
     } else {
-        if (fast) EQ_RUN(false, 0u, true); else EQ_RUN(false, 0u, false);
+        if (T.mode == M_ROW1) EQ_RUN(false, 0u, M_ROW1); else EQ_RUN(false, 0u, M_GENERAL);
     }
 #undef EQ_RUN
 }
@@ -602,17 +694,22 @@ eq_status launch_block(const eq_block *b, void *out, void *stream) {
             t.off_esc_val = h.off_esc_val;
             t.Z = h.chunk_symbols;
             t.dtype = h.dtype;
-            t.flags = 0;
+            t.is_const = 0;
             t.const_sym = 0;
             if (h.single_symbol >= 0) {
-                t.flags |= F_CONST;
+                t.is_const = 1;
                 t.const_sym = (uint32_t)h.single_symbol;
             }
             const uint32_t vec = BF16 ? 2u * (K < 8 ? K : 8u) : K;  // bytes per store
             const uint64_t elem = BF16 ? 2u : 1u;
             const bool aligned = ((obase + r.out_offset * elem) % vec) == 0;
-            const bool rows_ok = !BF16 || (h.cols % K == 0 && h.cols >= 64u * K);
-            if (aligned && rows_ok) t.flags |= F_FAST;
+            const uint64_t G = 64u * K;
+            t.mode = M_GENERAL;
+            if (aligned && !BF16) t.mode = M_ROW1;
+            if (aligned && BF16 && h.cols < (1ull << 31)) {
+                if (h.cols % G == 0) t.mode = M_ROW1;
+                else if (h.cols >= G && h.cols % K == 0) t.mode = M_ROW2;
+            }
             t.wg_begin = (uint32_t)wgs;
             wgs += (h.n_chunks + kWaves - 1) / kWaves;
         }

@@ -19,7 +19,9 @@ import re
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libeq.so")
+# EQ_LIBRARY may name another build of the same library (e.g. a tuning build
+# with different compile-time parameters); the default is the in-tree build.
+LIB_PATH = os.environ.get("EQ_LIBRARY") or os.path.join(_HERE, "libeq.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "eq.h")
 
 EQ_OK, EQ_EINVAL, EQ_ERANGE, EQ_ECORRUPT, EQ_EHIP, EQ_EUNSUPPORTED, EQ_ENOMEM = 0, -1, -2, -3, -4, -5, -6
