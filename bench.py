@@ -136,30 +136,43 @@ def sampled_parity(cfg, layer, specs, conts, out, offs, rng_seed=1) -> int:
 
 
 def cpu_baseline(conts, target_s: float = 10.0):
-    """The oracle, as it stands, decoding + dequantising a bounded sample of
-    the same containers on the host cores (chunk-parallel)."""
+    """The oracle, as it stands, decoding + dequantising the same containers
+    on the host cores (chunk-parallel, static partition). The sample grows
+    from one chunk per thread per tensor up to the whole block, and the whole
+    block is decoded repeatedly when one pass takes less than target_s."""
     import numpy as np
     import oracle
     threads = host_cores()
-    sample = [(c, min(int(c.hdr.n_chunks), threads)) for c in conts]  # calibration: 1 chunk/thread
     outs = [np.zeros(int(c.hdr.n), np.uint16) for c in conts]
 
     def run(per_tensor):
         t0 = time.perf_counter()
         n = 0
-        for (c, _), k, o in zip(sample, per_tensor, outs):
+        for c, k, o in zip(conts, per_tensor, outs):
             flags = oracle.decode_chunks(c.host, 0, k, threads, bf16_out=o)
             if flags:
                 raise RuntimeError(f"oracle decode flags {flags}")
             n += min(int(c.hdr.n), k * int(c.hdr.chunk_symbols))
         return time.perf_counter() - t0, n
 
-    dt, n = run([k for _, k in sample])
-    scale = max(1.0, target_s / max(dt, 1e-3))
-    ks = [min(int(c.hdr.n_chunks), max(1, int(k * scale))) for c, k in sample]
+    ks = [min(int(c.hdr.n_chunks), threads) for c in conts]
     dt, n = run(ks)
-    desc = (f"chunks [0, k) of each of the 7 tensors, k = {ks}: {n} weights "
-            f"({n / 1e6:.1f} M), decoded + dequantised to bf16 by the oracle with {threads} threads")
+    scale = max(1.0, target_s / max(dt, 1e-3))
+    ks = [min(int(c.hdr.n_chunks), max(1, int(k * scale))) for c, k in zip(conts, ks)]
+    dt, n = run(ks)
+    reps = 1
+    if dt < target_s:
+        reps = max(1, int(target_s / max(dt, 1e-3)))
+        total_t, total_n = 0.0, 0
+        for _ in range(reps):
+            d, m = run(ks)
+            total_t += d
+            total_n += m
+        dt, n = total_t, total_n
+    whole = all(k == int(c.hdr.n_chunks) for c, k in zip(conts, ks))
+    what = "the whole 7-tensor block" if whole else f"chunks [0, k) of each tensor, k = {ks}"
+    desc = (f"{what} ({n // reps / 1e6:.1f} M weights per pass, {reps} pass(es)), decoded + "
+            f"dequantised to bf16 by the oracle with {threads} threads")
     return {"value": round(2.0 * n / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": desc, "seconds": round(dt, 2)}
 

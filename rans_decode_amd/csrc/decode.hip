@@ -49,6 +49,9 @@ namespace {
 #ifndef EQ_LUT8
 #define EQ_LUT8 1
 #endif
+#ifndef EQ_NT_STORES
+#define EQ_NT_STORES 1
+#endif
 constexpr int kWaves = EQ_WAVES;
 constexpr int kThreads = 64 * kWaves;
 constexpr uint32_t kRing = EQ_RING_WORDS;       // power of two
@@ -56,7 +59,8 @@ constexpr uint32_t kBlk = kRing / 2;            // words per refill
 constexpr uint32_t kLaneWords = kBlk / 64;      // words each lane loads per refill
 constexpr uint32_t kCheck = kBlk / 64;          // steps between refill checks
 constexpr uint32_t kRingAlloc = kRing + 64;     // + copy of the ring's first 64 words
-static_assert(kRing == 1024 || kRing == 512, "ring of 512 or 1024 words");
+static_assert(kRing == 2048 || kRing == 1024 || kRing == 512 || kRing == 256,
+              "ring of 256 to 2048 words");
 
 // Output modes of a tensor (host-chosen).
 enum : uint32_t {
@@ -175,8 +179,11 @@ __device__ void build_lut(const TArgs &T, LutEnt *lut, uint32_t *cum) {
 }
 
 template <uint32_t LW> struct LaneBlock;
+struct uint8x { uint4 a, b; };
+template <> struct LaneBlock<16> { using type = uint8x; };
 template <> struct LaneBlock<8> { using type = uint4; };
 template <> struct LaneBlock<4> { using type = uint2; };
+template <> struct LaneBlock<2> { using type = uint32_t; };
 using Blk = LaneBlock<kLaneWords>::type;
 
 __device__ __forceinline__ Blk load_block(const uint16_t *words, uint32_t b, uint32_t wpad,
@@ -393,9 +400,16 @@ struct Chunk {
             *reinterpret_cast<uint2 *>(dst) = make_uint2(pk[0], pk[1]);
         } else {
 #pragma unroll
-            for (int i = 0; i < K / 8; ++i)
+            for (int i = 0; i < K / 8; ++i) {
+#if EQ_NT_STORES
+                typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+                u32x4 v = {pk[4 * i], pk[4 * i + 1], pk[4 * i + 2], pk[4 * i + 3]};
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(dst) + i);
+#else
                 reinterpret_cast<uint4 *>(dst)[i] =
                     make_uint4(pk[4 * i], pk[4 * i + 1], pk[4 * i + 2], pk[4 * i + 3]);
+#endif
+            }
         }
     }
 
@@ -525,7 +539,6 @@ template <int K, bool BF16>
 __global__ void __launch_bounds__(kThreads) k_decode(LArgs a) {
     __shared__ LutEnt lut[4096];
     __shared__ __attribute__((aligned(16))) uint16_t rings[kWaves][kRingAlloc];
-    __shared__ uint32_t cum[260];
 
     const uint32_t wg = blockIdx.x;
     uint32_t ti = 0;
@@ -535,7 +548,9 @@ __global__ void __launch_bounds__(kThreads) k_decode(LArgs a) {
     const uint32_t lane = threadIdx.x & 63u;
     const uint64_t chunk = (uint64_t)(wg - T.wg_begin) * kWaves + wave;
     const bool is_const = T.is_const != 0;
-    if (!is_const) build_lut(T, lut, cum);
+    // the LUT build's cumulative-frequency scratch reuses the (not yet
+    // filled) rings
+    if (!is_const) build_lut(T, lut, reinterpret_cast<uint32_t *>(&rings[0][0]));
     if (chunk >= T.n_chunks) return;
     if (is_const) {
         const_chunk<BF16>(T, chunk, lane, a.out, a.status);
