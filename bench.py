@@ -197,14 +197,25 @@ def copy_ceiling(nbytes: int) -> float:
     return 2.0 * nbytes / (ms * 1e-3) / 1e9
 
 
+WORKLOADS = {
+    "block70b": (4, "70B-shaped block decode+dequant: q,o 8192x8192; k,v 1024x8192; gate,up 28672x8192; "
+                    "down 8192x28672; int8 2.1-bit Laplace codes, 4 super-weight escapes"),
+    "cfg1": (1, "single 1024x1024 int8 matrix, 2.1-bit Laplace codes"),
+    "cfg2": (2, "single 4096x4096 int8 matrix (7B q_proj), 3.0-bit Laplace codes"),
+    "cfg3": (3, "7B-shaped block decode+dequant: q,k,v,o 4096x4096; gate,up 11008x4096; down 4096x11008; "
+                "E4M3 codes at 2.1 bits"),
+}
+
+
 def bench_block(args):
     import numpy as np
     import torch
     import synth
     from rans_decode_amd import eq
 
+    cfg, what = WORKLOADS[args.workload]
     t0 = time.perf_counter()
-    specs, conts = build_block(4, 0, args.lane_run)
+    specs, conts = build_block(cfg, 0, args.lane_run)
     offs = synth.block_offsets(specs)
     n = offs[-1]
     log(f"block built in {time.perf_counter() - t0:.1f} s: {n} weights, "
@@ -219,7 +230,7 @@ def bench_block(args):
     torch.cuda.synchronize()
     if int(status.item()) != 0:
         raise RuntimeError(f"device status {int(status.item())}")
-    bad = sampled_parity(4, 0, specs, conts, out, offs[:-1])
+    bad = sampled_parity(cfg, 0, specs, conts, out, offs[:-1])
     log(f"sampled parity vs oracle: {bad} mismatching elements")
     if bad:
         raise RuntimeError("decoded output differs from the oracle")
@@ -244,7 +255,8 @@ def bench_block(args):
     traffic = traffic_record(os.path.join(ROOT, "rans_decode_amd", "csrc", "decode.hip"))
     total_container = sum(c.nbytes for c in conts)
     rec = {
-        "metric": "decoded weight GB/s (bf16 out) and % HBM roofline, 70B-shaped block decode",
+        "metric": "decoded weight GB/s (bf16 out) and % HBM roofline, 70B-shaped block decode"
+                  if cfg == 4 else f"decoded weight GB/s (bf16 out) and % HBM roofline, {args.workload}",
         "value": round(outb / (avg_ms * 1e-3) / 1e9, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -257,9 +269,7 @@ def bench_block(args):
         "dtype": "u32/f32",
         "data": "synthetic",
         "config": {
-            "workload": "70B-shaped block decode+dequant: q,o 8192x8192; k,v 1024x8192; "
-                        "gate,up 28672x8192; down 8192x28672; int8 2.1-bit Laplace codes, "
-                        f"64Ki-symbol chunks, 64 lanes, K={args.lane_run}, 4 super-weight escapes, bf16 out",
+            "workload": f"{what}; 64Ki-symbol chunks, 64 lanes, K={args.lane_run}, bf16 out",
             "weights": n,
             "container_bytes": total_container,
             "effective_bits_per_weight": round(8.0 * total_container / n, 4),
@@ -404,7 +414,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", choices=["block70b", "model80"], default="block70b")
+    ap.add_argument("--workload", choices=["block70b", "model80", "cfg1", "cfg2", "cfg3"],
+                    default="block70b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-ceiling", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -421,10 +432,10 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    if args.workload == "block70b":
-        bench_block(args)
-    else:
+    if args.workload == "model80":
         bench_model(args)
+    else:
+        bench_block(args)
 
 
 if __name__ == "__main__":
