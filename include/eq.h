@@ -201,6 +201,29 @@ eq_status eq_decode_block(const eq_block *b, uint8_t *d_symbols, void *stream);
 eq_status eq_decode_dequant_bf16(const eq_block *b, uint16_t *d_bf16, void *stream);
 
 /*
+ * eq_decode_gemv_bf16 -- fused decode + dequantisation + batch-1 GEMV for
+ * every tensor i of b: y_i[r] = sum_c W_i[r, c] * x_i[c], where W_i is
+ * exactly the bf16 matrix eq_decode_dequant_bf16 would write (scales, RNE,
+ * super weights), but is never written: each wave multiplies the weights it
+ * decodes by x in registers. This is the decompression fused into the
+ * matrix-multiply kernel that the EntQuant summary names as future work (its
+ * limitations / future-directions part); HBM traffic per weight falls from
+ * the compressed bytes + 2 B written + 2 B read back to the compressed bytes.
+ * d_x: host array of n_tensors device pointers, tensor i's bf16 input
+ *    [cols_i] (16-byte aligned). d_y: host array of n_tensors device
+ *    pointers, its fp32 output [rows_i]. tensors[i].out_offset is ignored.
+ * Requirements: chunk_symbols a multiple of cols (chunks hold whole rows) and
+ *    cols a multiple of lane_run; otherwise EQ_EUNSUPPORTED (encode with such
+ *    a chunk size, e.g. two 28672-column rows per chunk).
+ * Arithmetic: fp32 accumulation of exact bf16 x bf16 products (v_dot2 on
+ *    pairs, per-lane partials, fixed-order wave reduction): deterministic, but
+ *    not bit-reproducible against other summation orders.
+ * Errors: as eq_decode_block, plus EQ_EUNSUPPORTED.
+ */
+eq_status eq_decode_gemv_bf16(const eq_block *b, const uint16_t *const *d_x, float *const *d_y,
+                              void *stream);
+
+/*
  * eq_gemv_bf16 -- y[r] = sum_c W[r, c] * x[c] for a row-major bf16 [rows,
  * cols] matrix W and bf16 vector x, fp32 accumulation, fp32 y. The batch-1
  * forward consumer of a decoded buffer (the "forward kernels" that follow

@@ -53,6 +53,7 @@ def lib():
         "or_decode_symbols": (ctypes.c_int64, [_P, _U64, _P]),
         "or_decode_dequant": (ctypes.c_int64, [_P, _U64, _P]),
         "or_header_fields": (ctypes.c_int, [_P, _U64, _P]),
+        "or_gemv_f64": (None, [_P, _U64, _U64, _P, _P, _P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -198,3 +199,17 @@ def decode_chunks(container: np.ndarray, k_lo: int, k_hi: int, threads: int,
     if flags < 0:
         raise OracleError(f"or_decode_chunks: {flags}")
     return int(flags)
+
+
+def gemv_f64(w_bits: np.ndarray, x_bits: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """y = W @ x in binary64 for bf16 bit patterns W [rows, cols] and x [cols];
+    also sum_c |W[r, c] x[c]| per row."""
+    w = np.ascontiguousarray(w_bits, dtype=np.uint16)
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    rows, cols = w.shape
+    if x.shape != (cols,):
+        raise ValueError("x must have one entry per column")
+    y = np.empty(rows, np.float64)
+    a = np.empty(rows, np.float64)
+    lib().or_gemv_f64(_ptr(w), rows, cols, _ptr(x), _ptr(y), _ptr(a))
+    return y, a

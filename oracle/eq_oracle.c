@@ -696,3 +696,37 @@ int or_header_fields(const uint8_t *buf, uint64_t len, uint64_t v[19]) {
 void or_bf16_rne_array(const float *v, uint64_t n, uint16_t *out) {
     for (uint64_t i = 0; i < n; i++) out[i] = or_bf16_rne(v[i]);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Batch-1 GEMV over decoded weights.                                        */
+/* ------------------------------------------------------------------------ */
+/* [EQ] section 2, technical component 3: the decoded bf16 weights feed the
+ * block's forward kernels; its limitations / future-work part proposes
+ * fusing the decompression into the matrix-multiply kernel. For one token
+ * that product is y[r] = sum_c W[r][c] * x[c] over a row-major [rows][cols]
+ * bf16 W and a bf16 x. Here in binary64: a bf16 x bf16 product has at most
+ * 16 significant bits, so every product is exact in double, and the sum in
+ * ascending c is within (cols - 1) * 2^-53 * sum |W x| of the exact value.
+ * absdot[r] = sum_c |W[r][c] * x[c]| (the scale of a summation-order error
+ * bound). bf16 bits widen to binary32 by a 16-bit shift (the format is the
+ * upper half of binary32). */
+static double bf16_to_double(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+void or_gemv_f64(const uint16_t *w, uint64_t rows, uint64_t cols, const uint16_t *x, double *y,
+                 double *absdot) {
+    for (uint64_t r = 0; r < rows; r++) {
+        double s = 0.0, a = 0.0;
+        for (uint64_t c = 0; c < cols; c++) {
+            const double p = bf16_to_double(w[r * cols + c]) * bf16_to_double(x[c]);
+            s += p;
+            a += p < 0 ? -p : p;
+        }
+        y[r] = s;
+        if (absdot) absdot[r] = a;
+    }
+}

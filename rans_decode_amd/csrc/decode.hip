@@ -75,6 +75,8 @@ struct TArgs {
     uint64_t off_scales, off_dir, off_states, off_words, off_esc_idx, off_esc_val, off_freq;
     uint32_t Z, dtype, mode, const_sym;
     uint32_t is_const, wg_begin;
+    const uint16_t *x;  // fused GEMV: the tensor's bf16 input vector [cols]
+    float *y;           // fused GEMV: its fp32 output [rows]
 };
 
 struct LArgs {
@@ -92,6 +94,54 @@ typedef float floatx2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     floatx2 f = {a, b};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
+// acc + w.lo * x.lo + w.hi * x.hi for two packed bf16 pairs (fp32 result).
+__device__ __forceinline__ float dot2_bf16(uint32_t w, uint32_t x, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, x),
+                                           acc, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 64 lanes (all active), fixed order: quad butterflies, half-row
+// and row mirrors (DPP), then the four row sums in lane order. Every lane
+// gets the same value.
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp_f<0x141>(v);  // row_half_mirror
+    v += dpp_f<0x140>(v);  // row_mirror
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return ((r0 + r1) + r2) + r3;
+}
+
+// A lane's K consecutive bf16 inputs of the fused GEMV, as packed pairs.
+template <int K> struct XRun { uint32_t p[(K + 1) / 2]; };
+template <int K>
+__device__ __forceinline__ XRun<K> load_x(const uint16_t *x) {
+    XRun<K> r;
+    if constexpr (K == 1) {
+        r.p[0] = *x;
+    } else if constexpr (K == 2) {
+        r.p[0] = *reinterpret_cast<const uint32_t *>(x);
+    } else if constexpr (K == 4) {
+        const uint2 v = *reinterpret_cast<const uint2 *>(x);
+        r.p[0] = v.x; r.p[1] = v.y;
+    } else {
+#pragma unroll
+        for (int i = 0; i < K / 8; ++i) {
+            const uint4 v = reinterpret_cast<const uint4 *>(x)[i];
+            r.p[4 * i] = v.x; r.p[4 * i + 1] = v.y; r.p[4 * i + 2] = v.z; r.p[4 * i + 3] = v.w;
+        }
+    }
+    return r;
 }
 
 #if EQ_LUT8
@@ -206,7 +256,7 @@ __device__ __forceinline__ void put_block(uint16_t *ring, uint32_t b, Blk v, uin
 
 // Per-chunk decoder state of one wave. Positions inside the chunk are u32
 // (a chunk holds at most 2^24 symbols); wave-uniform values stay in SGPRs.
-template <int K, bool BF16, uint32_t DT, int MODE>
+template <int K, bool BF16, uint32_t DT, int MODE, bool GEMV = false>
 struct Chunk {
     const TArgs &T;
     const LutEnt *lut;
@@ -231,6 +281,12 @@ struct Chunk {
     const uint64_t *eidx;
     const uint16_t *eval;
     char *ob;             // output of the chunk's first symbol
+    // fused GEMV (the chunk starts at a row boundary and holds whole rows)
+    const uint16_t *xv;   // the tensor's input vector
+    float *yv;            // the tensor's output vector
+    uint64_t row0;        // first row of the chunk
+    float acc;            // row-uniform groups: this lane's partial of the current row
+    float racc;           // other groups: running sum of the current row (wave-uniform)
 
     static constexpr uint32_t G = 64u * K;  // symbols per group of K steps
 
@@ -293,11 +349,29 @@ struct Chunk {
     __device__ __forceinline__ void group(uint32_t g, void *out) {
         const uint32_t g0 = g * G;                        // chunk-local group start
         const uint32_t q0 = g0 + lane * (uint32_t)K;      // this lane's first position
+        XRun<K> xr{};
+        uint32_t rl = 0;  // GEMV: chunk-local row of this lane's run
+        if constexpr (GEMV) {
+            // the run's inputs, fetched before the K steps hide their latency
+            // (a lane's run lies in one row; lanes past the chunk load nothing)
+            uint32_t c;
+            if constexpr (MODE == M_ROW1) {
+                c = col + lane * (uint32_t)K;
+            } else {
+                rl = q0 / cols32;
+                c = q0 - rl * cols32;
+            }
+            if (q0 < nk) xr = load_x<K>(xv + c);
+        }
         uint32_t ent[K];
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             if ((k & (kCheck - 1)) == 0) refill();
             ent[k] = step<MASKED>(q0 + (uint32_t)k < nk);
+        }
+        if constexpr (GEMV) {
+            gemv_group(g0, q0, rl, ent, xr);
+            return;
         }
         if constexpr (BF16) {
             uint16_t *ob = reinterpret_cast<uint16_t *>(this->ob);
@@ -353,10 +427,60 @@ struct Chunk {
         }
     }
 
+    // Fused GEMV epilogue of group g0: the lane's K weights exactly as the
+    // bf16 decode would store them (scale, RNE, super weights), dotted with
+    // its K inputs; row-uniform groups keep a per-lane partial until the row
+    // ends, other groups reduce every row they touch at once.
+    __device__ __forceinline__ void gemv_group(uint32_t g0, uint32_t q0, uint32_t rl, const uint32_t *ent,
+                                               const XRun<K> &xr) {
+        const bool valid = q0 < nk;
+        float s;
+        if constexpr (MODE == M_ROW1) {
+            s = s_cur;
+        } else {
+            const uint64_t r = row0 + rl;
+            s = scales[r < rows ? r : rows - 1];
+        }
+        uint32_t pk[(K + 1) / 2];
+#pragma unroll
+        for (int k = 0; k < K; k += 2) {
+            const float v0 = sym_value<DT>(ent[k]) * s;
+            const float v1 = (k + 1 < K) ? sym_value<DT>(ent[k + 1]) * s : 0.0f;
+            pk[k / 2] = pack_bf16(v0, v1);
+        }
+        if (esc_loc < g0 + G) patch_packed(g0, pk);
+        if constexpr (MODE == M_ROW1) {
+            float a = acc;
+#pragma unroll
+            for (int i = 0; i < (K + 1) / 2; ++i) a = dot2_bf16(pk[i], xr.p[i], a);
+            acc = valid ? a : acc;
+            advance_row();
+        } else {
+            float d = 0.0f;
+#pragma unroll
+            for (int i = 0; i < (K + 1) / 2; ++i) d = dot2_bf16(pk[i], xr.p[i], d);
+            d = valid ? d : 0.0f;
+            const uint32_t end = g0 + G < nk ? g0 + G : nk;
+            const uint32_t r_first = g0 / cols32, r_last = (end - 1u) / cols32;
+            for (uint32_t r = r_first; r <= r_last; ++r) {
+                racc += wave_sum(rl == r ? d : 0.0f);
+                if ((r + 1u) * cols32 <= end) {
+                    if (lane == 0) yv[row0 + r] = racc;
+                    racc = 0.0f;
+                }
+            }
+        }
+    }
+
     __device__ __forceinline__ void advance_row() {
         if constexpr (BF16 && MODE == M_ROW1) {
             col += G;
             if (col == cols32) {
+                if constexpr (GEMV) {
+                    const float t = wave_sum(acc);
+                    if (lane == 0) yv[row] = t;
+                    acc = 0.0f;
+                }
                 col = 0;
                 ++row;
                 s_cur = row_scale(row);
@@ -461,7 +585,16 @@ struct Chunk {
         scales = reinterpret_cast<const float *>(T.base + T.off_scales);
         eidx = reinterpret_cast<const uint64_t *>(T.base + T.off_esc_idx);
         eval = reinterpret_cast<const uint16_t *>(T.base + T.off_esc_val);
-        ob = static_cast<char *>(out) + (T.out_offset + p0) * (BF16 ? 2u : 1u);
+        if constexpr (GEMV) {
+            xv = T.x;
+            yv = T.y;
+            row0 = p0 / cols;
+            acc = 0.0f;
+            racc = 0.0f;
+            ob = nullptr;
+        } else {
+            ob = static_cast<char *>(out) + (T.out_offset + p0) * (BF16 ? 2u : 1u);
+        }
         if constexpr (BF16 && MODE != M_GENERAL) {
             row = p0 / cols;
             col = (uint32_t)(p0 - row * cols);
@@ -535,8 +668,49 @@ __device__ void const_chunk(const TArgs &T, uint64_t chunk, uint32_t lane, void 
     }
 }
 
-template <int K, bool BF16>
+// One-symbol tensor, fused GEMV: per row, lanes stride over the columns with
+// the row's weight (super weights substituted where listed), then reduce.
+__device__ void const_chunk_gemv(const TArgs &T, uint64_t chunk, uint32_t lane, uint32_t *status) {
+    const uint64_t p0 = chunk * T.Z;
+    const uint32_t nk = (uint32_t)umin64(T.Z, T.n - p0);
+    const uint8_t *dir = T.base + T.off_dir + chunk * 16u;
+    const uint32_t wc = *reinterpret_cast<const uint32_t *>(dir + 8);
+    const uint32_t xs = reinterpret_cast<const uint32_t *>(T.base + T.off_states)[chunk * 64u + lane];
+    const uint64_t bad = __builtin_amdgcn_ballot_w64(xs != 65536u);
+    raise_flag(status, (bad || wc) ? EQ_DEV_BAD_END_STATE : 0u, lane);
+    const float *sc = reinterpret_cast<const float *>(T.base + T.off_scales);
+    const uint64_t *eidx = reinterpret_cast<const uint64_t *>(T.base + T.off_esc_idx);
+    const uint16_t *eval = reinterpret_cast<const uint16_t *>(T.base + T.off_esc_val);
+    const uint32_t bits = T.const_sym << kSymShift;
+    const float v = T.dtype == EQ_DTYPE_INT8 ? sym_value<EQ_DTYPE_INT8>(bits) : sym_value<EQ_DTYPE_E4M3>(bits);
+    const uint64_t cols = T.cols, row0 = p0 / cols, nrows = nk / cols;
+    // this lane's next super weight (lanes walk their own positions in order)
+    uint64_t e = 0, hi = T.n_esc;
+    while (e < hi) {
+        const uint64_t mid = (e + hi) >> 1;
+        if (eidx[mid] < p0) e = mid + 1; else hi = mid;
+    }
+    for (uint64_t r = 0; r < nrows; ++r) {
+        const uint32_t w = pack_bf16(v * sc[row0 + r], 0.0f) & 0xFFFFu;
+        float acc = 0.0f;
+        for (uint64_t c = lane; c < cols; c += 64u) {
+            const uint64_t pos = p0 + r * cols + c;
+            while (e < T.n_esc && eidx[e] < pos) ++e;
+            const uint32_t wb = (e < T.n_esc && eidx[e] == pos) ? eval[e] : w;
+            acc = dot2_bf16(wb, T.x[c], acc);
+        }
+        const float t = wave_sum(acc);
+        if (lane == 0) T.y[row0 + r] = t;
+    }
+}
+
+// Output kinds of the decode kernel.
+enum : int { OUT_U8 = 0, OUT_BF16 = 1, OUT_GEMV = 2 };
+
+template <int K, int OUT>
 __global__ void __launch_bounds__(kThreads) k_decode(LArgs a) {
+    constexpr bool BF16 = OUT != OUT_U8;
+    constexpr bool GEMV = OUT == OUT_GEMV;
     __shared__ LutEnt lut[4096];
     __shared__ __attribute__((aligned(16))) uint16_t rings[kWaves][kRingAlloc];
 
@@ -553,17 +727,26 @@ __global__ void __launch_bounds__(kThreads) k_decode(LArgs a) {
     if (!is_const) build_lut(T, lut, reinterpret_cast<uint32_t *>(&rings[0][0]));
     if (chunk >= T.n_chunks) return;
     if (is_const) {
-        const_chunk<BF16>(T, chunk, lane, a.out, a.status);
+        if constexpr (GEMV) const_chunk_gemv(T, chunk, lane, a.status);
+        else const_chunk<BF16>(T, chunk, lane, a.out, a.status);
         return;
     }
     const uint64_t p0 = chunk * T.Z;
     const uint32_t nk = (uint32_t)umin64(T.Z, T.n - p0);
 #define EQ_RUN(BF, DT, MO)                                                             \
     do {                                                                               \
-        Chunk<K, BF, DT, MO> c{T, lut, rings[wave], lane, p0, nk};                     \
+        Chunk<K, BF, DT, MO, GEMV> c{T, lut, rings[wave], lane, p0, nk};               \
         c.run(chunk, a.out, a.status);                                                 \
     } while (0)
-    if constexpr (BF16) {
+    if constexpr (GEMV) {
+        if (T.dtype == EQ_DTYPE_INT8) {
+            if (T.mode == M_ROW1) EQ_RUN(true, EQ_DTYPE_INT8, M_ROW1);
+            else EQ_RUN(true, EQ_DTYPE_INT8, M_GENERAL);
+        } else {
+            if (T.mode == M_ROW1) EQ_RUN(true, EQ_DTYPE_E4M3, M_ROW1);
+            else EQ_RUN(true, EQ_DTYPE_E4M3, M_GENERAL);
+        }
+    } else if constexpr (BF16) {
         if (T.dtype == EQ_DTYPE_INT8) {
             if (T.mode == M_ROW1) EQ_RUN(true, EQ_DTYPE_INT8, M_ROW1);
             else if (T.mode == M_ROW2) EQ_RUN(true, EQ_DTYPE_INT8, M_ROW2);
@@ -642,17 +825,16 @@ __global__ void k_bf16(const float *__restrict__ in, uint64_t n, uint16_t *__res
 // ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
-template <bool BF16>
 using KernelFn = void (*)(LArgs);
 
-template <bool BF16>
-KernelFn<BF16> pick_kernel(uint32_t K) {
+template <int OUT>
+KernelFn pick_kernel(uint32_t K) {
     switch (K) {
-        case 1: return k_decode<1, BF16>;
-        case 2: return k_decode<2, BF16>;
-        case 4: return k_decode<4, BF16>;
-        case 8: return k_decode<8, BF16>;
-        case 16: return k_decode<16, BF16>;
+        case 1: return k_decode<1, OUT>;
+        case 2: return k_decode<2, OUT>;
+        case 4: return k_decode<4, OUT>;
+        case 8: return k_decode<8, OUT>;
+        case 16: return k_decode<16, OUT>;
         default: return nullptr;
     }
 }
@@ -672,9 +854,15 @@ bool header_ok(const eq_header &h) {
            s.esc_val == h.off_esc_val && s.total == h.total_bytes;
 }
 
-template <bool BF16>
-eq_status launch_block(const eq_block *b, void *out, void *stream) {
-    if (!b || (b->n_tensors && !b->tensors) || (b->n_tensors && !out)) return EQ_EINVAL;
+// One launch per run of up to EQ_MAX_BLOCK_TENSORS consecutive tensors with
+// the same lane run. OUT_GEMV takes x[i] / y[i] per tensor instead of `out`.
+template <int OUT>
+eq_status launch_block(const eq_block *b, void *out, const uint16_t *const *x, float *const *y,
+                       void *stream) {
+    constexpr bool BF16 = OUT != OUT_U8;
+    constexpr bool GEMV = OUT == OUT_GEMV;
+    if (!b || (b->n_tensors && !b->tensors)) return EQ_EINVAL;
+    if (b->n_tensors && (GEMV ? (!x || !y) : !out)) return EQ_EINVAL;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const uintptr_t obase = reinterpret_cast<uintptr_t>(out);
     uint32_t i = 0;
@@ -715,15 +903,28 @@ eq_status launch_block(const eq_block *b, void *out, void *stream) {
                 t.is_const = 1;
                 t.const_sym = (uint32_t)h.single_symbol;
             }
-            const uint32_t vec = BF16 ? 2u * (K < 8 ? K : 8u) : K;  // bytes per store
-            const uint64_t elem = BF16 ? 2u : 1u;
-            const bool aligned = ((obase + r.out_offset * elem) % vec) == 0;
             const uint64_t G = 64u * K;
-            t.mode = M_GENERAL;
-            if (aligned && !BF16) t.mode = M_ROW1;
-            if (aligned && BF16 && h.cols < (1ull << 31)) {
-                if (h.cols % G == 0) t.mode = M_ROW1;
-                else if (h.cols >= G && h.cols % K == 0) t.mode = M_ROW2;
+            t.x = nullptr;
+            t.y = nullptr;
+            if constexpr (GEMV) {
+                // chunks must hold whole rows and a lane's run one row
+                if (h.chunk_symbols % h.cols != 0 || h.cols % K != 0) return EQ_EUNSUPPORTED;
+                if (!x[i] || !y[i] || (reinterpret_cast<uintptr_t>(x[i]) & 15u) ||
+                    (reinterpret_cast<uintptr_t>(y[i]) & 3u))
+                    return EQ_EINVAL;
+                t.x = x[i];
+                t.y = y[i];
+                t.mode = h.cols % G == 0 ? M_ROW1 : M_GENERAL;
+            } else {
+                const uint32_t vec = BF16 ? 2u * (K < 8 ? K : 8u) : K;  // bytes per store
+                const uint64_t elem = BF16 ? 2u : 1u;
+                const bool aligned = ((obase + r.out_offset * elem) % vec) == 0;
+                t.mode = M_GENERAL;
+                if (aligned && !BF16) t.mode = M_ROW1;
+                if (aligned && BF16 && h.cols < (1ull << 31)) {
+                    if (h.cols % G == 0) t.mode = M_ROW1;
+                    else if (h.cols >= G && h.cols % K == 0) t.mode = M_ROW2;
+                }
             }
             t.wg_begin = (uint32_t)wgs;
             wgs += (h.n_chunks + kWaves - 1) / kWaves;
@@ -731,7 +932,7 @@ eq_status launch_block(const eq_block *b, void *out, void *stream) {
         a.n_tensors = nt;
         if (wgs > 0x7FFFFFFFull) return EQ_EINVAL;
         if (wgs) {
-            KernelFn<BF16> fn = pick_kernel<BF16>(K);
+            KernelFn fn = pick_kernel<OUT>(K);
             if (!fn) return EQ_EINVAL;
             hipLaunchKernelGGL(fn, dim3((uint32_t)wgs), dim3(kThreads), 0, s, a);
             if (hipGetLastError() != hipSuccess) return EQ_EHIP;
@@ -750,11 +951,16 @@ struct eq_pipeline {
 extern "C" {
 
 eq_status eq_decode_block(const eq_block *b, uint8_t *d_symbols, void *stream) {
-    return launch_block<false>(b, d_symbols, stream);
+    return launch_block<OUT_U8>(b, d_symbols, nullptr, nullptr, stream);
 }
 
 eq_status eq_decode_dequant_bf16(const eq_block *b, uint16_t *d_bf16, void *stream) {
-    return launch_block<true>(b, d_bf16, stream);
+    return launch_block<OUT_BF16>(b, d_bf16, nullptr, nullptr, stream);
+}
+
+eq_status eq_decode_gemv_bf16(const eq_block *b, const uint16_t *const *d_x, float *const *d_y,
+                              void *stream) {
+    return launch_block<OUT_GEMV>(b, nullptr, d_x, d_y, stream);
 }
 
 eq_status eq_gemv_bf16(const uint16_t *d_w, uint64_t rows, uint64_t cols, const uint16_t *d_x,

@@ -6,7 +6,7 @@ or cannot be loaded, importing this module raises.
 
 The functions keep the C names (``eq_build_tables``, ``eq_encode_host``,
 ``eq_parse_header``, ``eq_decode_block``, ``eq_decode_dequant_bf16``,
-``eq_gemv_bf16``, ``eq_pipeline_*``, ``eq_bf16_from_f32``) as thin wrappers
+``eq_decode_gemv_bf16``, ``eq_gemv_bf16``, ``eq_pipeline_*``, ``eq_bf16_from_f32``) as thin wrappers
 over numpy / torch arrays, plus a few conveniences (``build_tables``,
 ``encode_host``, ``DeviceContainer``, ``decode_dequant_bf16``, ...).
 """
@@ -72,6 +72,7 @@ def _load():
         "eq_parse_header": [_vp, _u64, P(eq_header)],
         "eq_decode_block": [P(eq_block), _vp, _vp],
         "eq_decode_dequant_bf16": [P(eq_block), _vp, _vp],
+        "eq_decode_gemv_bf16": [P(eq_block), _vp, _vp, _vp],
         "eq_gemv_bf16": [_vp, _u64, _u64, _vp, _vp, _vp],
         "eq_pipeline_create": [_u32, P(_vp)],
         "eq_pipeline_run": [_vp, P(eq_block), _u32, _vp, _vp, _vp, _vp, _vp, _vp],
@@ -252,6 +253,17 @@ class Block:
 def eq_decode_dequant_bf16(block: Block, out, stream=None) -> None:
     _check("eq_decode_dequant_bf16",
            _lib.eq_decode_dequant_bf16(ctypes.byref(block.c), out.data_ptr(), _stream_handle(stream)))
+
+
+def eq_decode_gemv_bf16(block: Block, xs, ys, stream=None) -> None:
+    """Fused decode + batch-1 GEMV: ys[i] (fp32 [rows_i]) = W_i @ xs[i] (bf16 [cols_i])."""
+    n = block.c.n_tensors
+    if len(xs) != n or len(ys) != n:
+        raise ValueError("one x and one y per tensor")
+    xa = (ctypes.c_void_p * max(n, 1))(*[x.data_ptr() for x in xs])
+    ya = (ctypes.c_void_p * max(n, 1))(*[y.data_ptr() for y in ys])
+    _check("eq_decode_gemv_bf16",
+           _lib.eq_decode_gemv_bf16(ctypes.byref(block.c), xa, ya, _stream_handle(stream)))
 
 
 def eq_decode_block(block: Block, out, stream=None) -> None:
