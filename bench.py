@@ -15,6 +15,7 @@ double-buffered decode + GEMV schedule and prints its own line.
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -74,10 +75,46 @@ def traffic_record(kernel_src: str):
         return None
 
 
-def build_block(cfg: int, layer: int = 0, lane_run: int = 8, use_cache: bool = True):
+def whole_row_chunk(cols: int, lane_run: int, target: int = 65536) -> int:
+    """Chunk size for the fused decode + GEMV: a multiple of both the row
+    length and 64 * K (so chunks hold whole rows), as close to target as
+    that allows."""
+    g = 64 * lane_run
+    lcm = cols * g // math.gcd(cols, g)
+    return lcm * max(1, round(target / lcm))
+
+
+VALU_PEAK_GINST = 256 * 4 * 2.4 / 4  # wave64 VALU instructions per ns: 256 CUs x 4 SIMDs, 4 cycles each, 2.4 GHz
+
+
+def counter_record(name: str, key: str, kernel_src: str):
+    """A per-launch figure measured with rocprofv3 counters (profiles/<name>),
+    if it was taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        line = line.split("#", 1)[0].strip()
+        if "=" in line:
+            k, v = (t.strip() for t in line.split("=", 1))
+            rec[k] = v
+    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    if rec.get("kernel_source_sha256") != sha:
+        return None
+    try:
+        return int(float(rec[key]))
+    except (KeyError, ValueError):
+        return None
+
+
+def build_block(cfg: int, layer: int = 0, lane_run: int = 8, use_cache: bool = True,
+                tensors=None, whole_rows: bool = False):
     """Encode one block with the library's host encoder and place its
-    containers in device memory. With EQ_BENCH_CACHE=<dir> the encoded
-    containers are kept there as .npy files and reused."""
+    containers in device memory (all tensors, or the listed indices). Chunks
+    are 64 Ki symbols, or with whole_rows the nearest multiple of the row
+    length (what the fused decode + GEMV needs). With EQ_BENCH_CACHE=<dir> the
+    encoded containers are kept there as .npy files and reused."""
     import numpy as np
     import synth
     from rans_decode_amd import eq
@@ -85,7 +122,10 @@ def build_block(cfg: int, layer: int = 0, lane_run: int = 8, use_cache: bool = T
     cache = os.environ.get("EQ_BENCH_CACHE") if use_cache else None
     conts = []
     for i, sp in enumerate(specs):
-        path = os.path.join(cache, f"cfg{cfg}_layer{layer}_t{i}_k{lane_run}.npy") if cache else None
+        if tensors is not None and i not in tensors:
+            continue
+        Z = whole_row_chunk(sp.cols, lane_run) if whole_rows else synth.CHUNK_SYMBOLS
+        path = os.path.join(cache, f"cfg{cfg}_layer{layer}_t{i}_k{lane_run}_z{Z}.npy") if cache else None
         if path and os.path.exists(path):
             blob = np.load(path)
         else:
@@ -95,7 +135,7 @@ def build_block(cfg: int, layer: int = 0, lane_run: int = 8, use_cache: bool = T
             blob = eq.encode_host(tab, sp.dtype, sp.rows, sp.cols, t.symbols, t.scales,
                                   t.esc_idx if esc else None, t.esc_val if esc else None,
                                   esc_code=t.esc_code if esc else 0,
-                                  chunk_symbols=synth.CHUNK_SYMBOLS, lane_run=lane_run)
+                                  chunk_symbols=Z, lane_run=lane_run)
             del t
             if path:
                 os.makedirs(cache, exist_ok=True)
@@ -104,34 +144,34 @@ def build_block(cfg: int, layer: int = 0, lane_run: int = 8, use_cache: bool = T
     return specs, conts
 
 
-def sampled_parity(cfg, layer, specs, conts, out, offs, rng_seed=1) -> int:
-    """Compare whole chunks (first, last and 3 random per tensor) with the
-    oracle's result computed from the regenerated original symbols; returns
-    the number of mismatching elements."""
+def sampled_symbols_check(cfg, layer, specs, conts, rng_seed=1) -> int:
+    """Decode-only pass (eq_decode_block, u8 codes) over the same containers;
+    whole chunks (first, last and 3 random per tensor) are compared with the
+    seeded generator's symbols. Returns the number of mismatching codes."""
     import numpy as np
     import torch
-    import oracle
     import synth
+    from rans_decode_amd import eq
+    offs = [0]
+    for sp in specs:
+        offs.append(offs[-1] + sp.n)
+    out = torch.empty(offs[-1], dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    eq.eq_decode_block(eq.Block(conts, offs[:-1], status), out)
+    torch.cuda.synchronize()
+    if int(status.item()) != 0:
+        raise RuntimeError(f"device status {int(status.item())}")
     rng = np.random.default_rng(rng_seed)
     bad = 0
     for i, (sp, c, o) in enumerate(zip(specs, conts, offs)):
-        scales = synth.scales_for(cfg, layer, i, sp.rows)
-        esc_idx, esc_val = synth.escapes_for(cfg, layer, i, sp)
         nch = int(c.hdr.n_chunks)
         Z = int(c.hdr.chunk_symbols)
         for k in sorted(set(rng.integers(0, nch, 3).tolist() + [0, nch - 1])):
             lo, hi = k * Z, min(sp.n, (k + 1) * Z)
-            r0 = lo // sp.cols
-            pad = lo - r0 * sp.cols
-            sym = np.concatenate([np.zeros(pad, np.uint8),
-                                  synth.symbols_slice(cfg, layer, i, lo, hi - lo, spec=sp)])
-            sym = np.concatenate([sym, np.zeros((-sym.size) % sp.cols, np.uint8)])
-            m = (esc_idx >= lo) & (esc_idx < hi)
-            exp = oracle.dequant_direct(sp.dtype, sym, sp.cols, scales[r0:r0 + sym.size // sp.cols],
-                                        esc_idx[m] - np.uint64(r0 * sp.cols), esc_val[m])
-            exp = exp[pad:pad + hi - lo]
-            got = out[o + lo:o + hi].view(torch.int16).cpu().numpy().view(np.uint16)
+            exp = synth.symbols_slice(cfg, layer, i, lo, hi - lo, spec=sp)
+            got = out[o + lo:o + hi].cpu().numpy()
             bad += int((got != exp).sum())
+    del out
     return bad
 
 
@@ -230,10 +270,10 @@ def bench_block(args):
     torch.cuda.synchronize()
     if int(status.item()) != 0:
         raise RuntimeError(f"device status {int(status.item())}")
-    bad = sampled_parity(cfg, 0, specs, conts, out, offs[:-1])
-    log(f"sampled parity vs oracle: {bad} mismatching elements")
+    bad = sampled_symbols_check(cfg, 0, specs, conts)
+    log(f"sampled decode check vs the generated symbols: {bad} mismatching codes")
     if bad:
-        raise RuntimeError("decoded output differs from the oracle")
+        raise RuntimeError("decoded symbols differ from the encoded ones")
 
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
@@ -277,7 +317,7 @@ def bench_block(args):
             "parallelism": "1 GPU",
         },
         "kernel_ms": {"mean": round(avg_ms, 4), "median": round(float(np.median(ms)), 4),
-                      "min": round(float(np.min(ms)), 4)},
+                      "min": round(float(np.min(ms)), 4), "all": [round(x, 4) for x in ms]},
         "compressed_read_GBps": round(comp / (avg_ms * 1e-3) / 1e9, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
@@ -289,6 +329,122 @@ def bench_block(args):
         rec["frac_of_copy_ceiling"] = round(achieved / cc, 4)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(conts, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+def gemv_bound(w_bf16, x_bf16):
+    """2 * cols * 2^-23 * sum_c |W[r, c] x[c]| per row: twice the fp32
+    summation bound, since both compared results carry one."""
+    import torch
+    a = w_bf16.float().abs() @ x_bf16.float().abs()
+    return 2.0 * w_bf16.shape[1] * 2.0**-23 * a
+
+
+def bench_gemv(args):
+    """Fused decode + batch-1 GEMV of the 70B-shaped block (whole-row chunks:
+    64 Ki symbols, two 28,672-column rows for down), one eq_decode_gemv_bf16
+    call per step over the 7 tensors; next to it the unfused path (decode to
+    bf16, then 7 GEMVs) and the GEMVs alone over the bf16 weights."""
+    import numpy as np
+    import torch
+    import synth
+    from rans_decode_amd import eq
+
+    t0 = time.perf_counter()
+    specs, conts = build_block(4, 0, args.lane_run, whole_rows=True)
+    offs = synth.block_offsets(specs)
+    n = offs[-1]
+    log(f"block built in {time.perf_counter() - t0:.1f} s (whole-row chunks)")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    block = eq.Block(conts, offs[:-1], status)
+    xs = [torch.from_numpy(synth.gemv_activation(4, 0, i, sp.cols)).to(torch.bfloat16).cuda()
+          for i, sp in enumerate(specs)]
+    ys = [torch.empty(sp.rows, dtype=torch.float32, device="cuda") for sp in specs]
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        eq.eq_decode_gemv_bf16(block, xs, ys, stream)
+    torch.cuda.synchronize()
+    if int(status.item()) != 0:
+        raise RuntimeError(f"device status {int(status.item())}")
+    bad = sampled_symbols_check(4, 0, specs, conts)
+    if bad:
+        raise RuntimeError("decoded symbols differ from the encoded ones")
+
+    # the unfused path on the same containers, and the product check
+    buf = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    y_ref = [torch.empty_like(y) for y in ys]
+
+    def unfused(gemv_only=False):
+        if not gemv_only:
+            eq.eq_decode_dequant_bf16(block, buf, stream)
+        for i, (sp, o) in enumerate(zip(specs, offs)):
+            eq.eq_gemv_bf16(buf.view(torch.int16), sp.rows, sp.cols, xs[i].view(torch.int16), y_ref[i],
+                            stream, w_offset_elems=o)
+
+    unfused()
+    torch.cuda.synchronize()
+    worst = 0.0
+    for i, (sp, o) in enumerate(zip(specs, offs)):
+        w = buf[o:o + sp.n].view(sp.rows, sp.cols)
+        tol = gemv_bound(w, xs[i])
+        ratio = float(((ys[i] - y_ref[i]).abs() / tol.clamp_min(1e-30)).max())
+        worst = max(worst, ratio)
+        del w, tol
+    if worst > 1.0:
+        raise RuntimeError(f"fused GEMV differs from decode + GEMV beyond the fp32 bound ({worst:.3f})")
+    log(f"fused vs unfused outputs: worst |diff| / bound = {worst:.4f}")
+
+    def timed(fn):
+        ms = []
+        for _ in range(args.steps):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record(stream)
+            fn()
+            e.record(stream)
+            torch.cuda.synchronize()
+            ms.append(s.elapsed_time(e))
+        return ms
+
+    wall0 = time.perf_counter()
+    fused_ms = timed(lambda: eq.eq_decode_gemv_bf16(block, xs, ys, stream))
+    wall = time.perf_counter() - wall0
+    unfused_ms = timed(unfused)
+    gemv_ms = timed(lambda: unfused(gemv_only=True))
+    if int(status.item()) != 0:
+        raise RuntimeError(f"device status {int(status.item())}")
+    f = float(np.mean(fused_ms))
+    comp, _ = algorithmic_bytes(conts)
+    xy = sum(2 * sp.cols + 4 * sp.rows for sp in specs)
+    valu = counter_record("decode_gemv70b_counters.txt", "valu_wave_instructions_per_launch",
+                          os.path.join(ROOT, "rans_decode_amd", "csrc", "decode.hip"))
+    roof = {"bound": "alu", "achieved": None, "peak": VALU_PEAK_GINST, "unit": "Ginst/s",
+            "frac": None, "traffic": None,
+            "hbm_GBps": round((comp + xy) / (f * 1e-3) / 1e9, 1),
+            "hbm_frac": round((comp + xy) / (f * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    if valu:
+        ach = valu / (f * 1e-3) / 1e9
+        roof.update(achieved=round(ach, 2), frac=round(ach / VALU_PEAK_GINST, 4))
+    rec = {
+        "metric": "fused decode + batch-1 GEMV of the 70B-shaped block (weights never written)",
+        "value": round(f, 4), "unit": "ms/block", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "u32/f32",
+        "data": "synthetic",
+        "config": {"workload": "70B-shaped block (q,o 8192x8192; k,v 1024x8192; gate,up 28672x8192; "
+                               "down 8192x28672; int8 2.1-bit codes, 4 super weights) with whole-row "
+                               f"chunks, K={args.lane_run}; x ~ N(0,1) in bf16, y fp32",
+                   "weights": n, "chunk_symbols": [int(c.hdr.chunk_symbols) for c in conts],
+                   "parallelism": "1 GPU"},
+        "kernel_ms": {"mean": round(f, 4), "median": round(float(np.median(fused_ms)), 4),
+                      "min": round(float(np.min(fused_ms)), 4)},
+        "weights_per_s_G": round(n / (f * 1e-3) / 1e9, 1),
+        "unfused_decode_then_gemv_ms": round(float(np.mean(unfused_ms)), 4),
+        "bf16_resident_gemv_ms": round(float(np.mean(gemv_ms)), 4),
+        "speedup_vs_unfused": round(float(np.mean(unfused_ms)) / f, 3),
+        "ratio_vs_bf16_resident": round(f / float(np.mean(gemv_ms)), 3),
+        "roofline": roof,
+        "fused_vs_unfused_worst_over_bound": round(worst, 5),
+    }
     print(json.dumps(rec), flush=True)
 
 
@@ -380,11 +536,45 @@ def bench_model(args):
         raise RuntimeError("pipeline GEMV outputs differ from the bf16-resident GEMVs")
     bad = 0
     for b in range(0, L, max(1, L // 8)):
-        bad += sampled_parity(5, b, specs, blocks[b].containers,
-                              resident[b * nblk:(b + 1) * nblk], offs[:-1], rng_seed=b)
+        bad += sampled_symbols_check(5, b, specs, blocks[b].containers, rng_seed=b)
     if bad:
-        raise RuntimeError(f"sampled parity: {bad} mismatching elements")
-    log(f"pipeline GEMV outputs identical to resident GEMVs; sampled parity 0 mismatches")
+        raise RuntimeError(f"sampled decode check: {bad} mismatching codes")
+    log(f"pipeline GEMV outputs identical to resident GEMVs; sampled decode check 0 mismatches")
+
+    # fused decode + GEMV per token (one stream): down_proj re-encoded with
+    # whole-row chunks, the other six containers shared
+    t1 = time.perf_counter()
+    fblocks = []
+    for layer in range(L):
+        _, dconts = build_block(5, layer, args.lane_run, use_cache=False, tensors=[6], whole_rows=True)
+        fblocks.append(eq.Block(blocks[layer].containers[:6] + dconts, offs[:-1], None))
+    log(f"whole-row down_proj containers built in {time.perf_counter() - t1:.0f} s")
+    yf = [[torch.empty_like(y) for y in yl] for yl in ys]
+
+    def fused_token():
+        for b in range(L):
+            eq.eq_decode_gemv_bf16(fblocks[b], xs[b], yf[b], ds)
+
+    fused_token()
+    torch.cuda.synchronize()
+    worst = 0.0
+    for b in sorted({0, L // 2, L - 1}):
+        for i, (sp, o) in enumerate(zip(specs, offs)):
+            w = resident[b * nblk + o:b * nblk + o + sp.n].view(sp.rows, sp.cols)
+            tol = gemv_bound(w, xs[b][i])
+            worst = max(worst, float(((yf[b][i] - y_res[b][i]).abs() / tol.clamp_min(1e-30)).max()))
+            del w, tol
+    if worst > 1.0:
+        raise RuntimeError(f"fused GEMV differs from the resident GEMV beyond the fp32 bound ({worst:.3f})")
+    fused_ms = []
+    for _ in range(args.steps):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(ds)
+        fused_token()
+        e.record(ds)
+        torch.cuda.synchronize()
+        fused_ms.append(s.elapsed_time(e))
+    fus = float(np.median(fused_ms))
     tok = float(np.median(tok_ms))
     res = float(np.median(res_ms))
     dec_bytes = 2 * nblk * L
@@ -404,6 +594,10 @@ def bench_model(args):
         "bf16_resident_gemv_ms_per_token": round(res, 3),
         "slowdown_vs_bf16_resident": round(tok / res, 3),
         "token_ms_all": [round(x, 3) for x in tok_ms],
+        "fused_decode_gemv_ms_per_token": round(fus, 3),
+        "fused_ratio_vs_bf16_resident": round(fus / res, 3),
+        "fused_speedup_vs_pipeline": round(tok / fus, 3),
+        "fused_vs_resident_worst_over_bound": round(worst, 5),
     }
     print(json.dumps(rec), flush=True)
     pipe.close()
@@ -414,7 +608,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", choices=["block70b", "model80", "cfg1", "cfg2", "cfg3"],
+    ap.add_argument("--workload", choices=["block70b", "model80", "gemv70b", "cfg1", "cfg2", "cfg3"],
                     default="block70b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-ceiling", action="store_true")
@@ -434,6 +628,8 @@ def main():
         sys.exit(1)
     if args.workload == "model80":
         bench_model(args)
+    elif args.workload == "gemv70b":
+        bench_gemv(args)
     else:
         bench_block(args)
 
