@@ -16,9 +16,10 @@
  *  - technical component 4 (super weights): extreme outliers are excluded
  *    from the entropy-optimised stream (Int8 base format).
  * "EntroLLM: Entropy Encoded Weight Compression for Efficient Large Language
- * Model Inference on Edge Devices", technical overview, method item 3: the
- * coded parameter space is split into chunks that keep the tensor structure
- * and are decoded independently and concurrently.
+ * Model Inference on Edge Devices", technical overview, method item 2: the
+ * quantised weights are Huffman-coded (frequent values get short codes);
+ * method item 3: the coded parameter space is split into chunks that keep
+ * the tensor structure and are decoded independently and concurrently.
  *
  * So: byte symbols + a frequency table + per-row fp32 scales in, a bf16
  * [rows, cols] weight matrix out, with
@@ -56,6 +57,22 @@
  *  - super weights: the stream holds the escape code exactly at the listed
  *    flat indices (the code is coded like any symbol); decode writes the
  *    listed bf16 bits there.
+ *  - header offset 144, u32 codec: 0 = the rANS coder above; 1 = Huffman
+ *    (EntroLLM's coder, same chunks, lanes, sections and outputs):
+ *      - the freq section holds code lengths (u16: 0 absent, 1..12 bits, or
+ *        0x100 for a lone symbol coded in zero bits); probability bits
+ *        (offset 44) = 12, the longest codeword; no states section (size 0);
+ *      - lengths: optimal prefix code over the exact symbol counts with
+ *        codewords of at most 12 bits (package-merge; coins sorted by
+ *        (count, byte), a coin before a package of equal weight);
+ *        canonical codewords in (length, byte) order;
+ *      - each lane's bitstream is its codewords, most significant bit
+ *        first, packed into 16-bit words from bit 0 up; at every step each
+ *        active lane holding fewer than 12 bits first takes the next word
+ *        of the chunk (lanes in ascending order; zero words once its
+ *        bitstream has ended), then every active lane decodes one codeword;
+ *      - a chunk is valid iff all its words are taken and every lane's
+ *        leftover bits are zero.
  *
  * CONVENTIONS
  *  - Every function returns an eq_status; no exception crosses the ABI.
@@ -92,6 +109,10 @@ typedef int32_t eq_status;
 #define EQ_DTYPE_INT8 1u /* two's-complement int8 codes */
 #define EQ_DTYPE_E4M3 2u /* OCP FP8 E4M3FN codes */
 
+#define EQ_CODEC_RANS 0u    /* container codec: interleaved rANS (EntQuant's ANS) */
+#define EQ_CODEC_HUFFMAN 1u /* container codec: interleaved canonical Huffman (EntroLLM) */
+#define EQ_HUFF_MAX_LEN 12u /* longest Huffman codeword, bits */
+
 #define EQ_LANES 64u
 #define EQ_MAX_BLOCK_TENSORS 16u /* tensors per kernel launch (more: several launches) */
 
@@ -111,7 +132,7 @@ typedef struct eq_tensor_desc {
     uint32_t chunk_symbols; /* Z: multiple of 64*K, at most 2^24 */
     uint32_t esc_enabled;   /* 1: stream carries super-weight escapes */
     uint32_t esc_code;      /* the escape byte (used when esc_enabled) */
-    uint32_t reserved;      /* 0 */
+    uint32_t codec;         /* EQ_CODEC_RANS (0) or EQ_CODEC_HUFFMAN */
 } eq_tensor_desc;
 
 /* Parsed, validated container header (host copy). */
@@ -119,7 +140,9 @@ typedef struct eq_header {
     uint32_t dtype, flags, chunk_symbols, lane_run;
     uint64_t rows, cols, n, n_chunks, n_esc, n_words;
     uint32_t esc_code;
-    int32_t single_symbol; /* byte of a one-symbol tensor (f = 4096), else -1 */
+    int32_t single_symbol; /* byte of a one-symbol tensor (f = 4096 / zero-bit code), else -1 */
+    uint32_t codec;        /* EQ_CODEC_RANS or EQ_CODEC_HUFFMAN */
+    uint32_t reserved;     /* 0 */
     uint64_t off_freq, off_scales, off_dir, off_states, off_words, off_esc_idx, off_esc_val;
     uint64_t total_bytes;
 } eq_header;
@@ -154,7 +177,9 @@ eq_status eq_build_tables(const uint8_t *symbols, uint64_t n, eq_tables *out);
  * (technical component 2 of the EntQuant summary: flatten, ANS-compress,
  * store bitstream + scales + metadata). Host only, multi-threaded over chunks.
  * t: tables whose freq covers every symbol present (eq_build_tables output or
- *    any valid table); d: shape and layout; symbols: rows*cols bytes; scales:
+ *    any valid table); with d->codec = EQ_CODEC_HUFFMAN the code lengths are
+ *    derived from t->counts instead (EntroLLM method item 2), so every
+ *    present symbol needs a nonzero count; d: shape and layout; symbols: rows*cols bytes; scales:
  *    rows finite fp32; esc_idx / esc_bf16: n_esc strictly ascending flat
  *    indices and their bf16 bits (NULL when n_esc == 0).
  * out / cap: caller's buffer. If out is NULL or cap is too small the call
@@ -164,7 +189,8 @@ eq_status eq_build_tables(const uint8_t *symbols, uint64_t n, eq_tables *out);
  *    an escape list that does not match the escape-code positions (or
  *    escapes without esc_enabled); an E4M3 NaN code outside the escapes; a
  *    non-finite scale; K not in {1,2,4,8,16}; Z not a multiple of 64*K or
- *    above 2^24; rows or cols 0. EQ_ENOMEM if scratch allocation fails.
+ *    above 2^24; rows or cols 0; an unknown codec. EQ_ENOMEM if scratch
+ *    allocation fails.
  */
 eq_status eq_encode_host(const eq_tables *t, const eq_tensor_desc *d, const uint8_t *symbols,
                          const float *scales, const uint64_t *esc_idx, const uint16_t *esc_bf16,

@@ -48,6 +48,11 @@ def lib():
         "or_encode": (ctypes.c_int, [_U32, _U64, _U64, _P, _P, _P, _U32, _U32, _U32,
                                      ctypes.c_uint8, _P, _P, _U64,
                                      ctypes.POINTER(_P), ctypes.POINTER(_U64)]),
+        "or_encode_codec": (ctypes.c_int, [_U32, _U32, _U64, _U64, _P, _P, _P, _U32, _U32, _U32,
+                                           ctypes.c_uint8, _P, _P, _U64,
+                                           ctypes.POINTER(_P), ctypes.POINTER(_U64)]),
+        "or_huff_lengths": (ctypes.c_int, [_P, _U32, _P]),
+        "or_huff_codes": (ctypes.c_int, [_P, _P]),
         "or_free": (None, [_P]),
         "or_decode_chunks": (ctypes.c_int64, [_P, _U64, _U64, _U64, _U32, _P, _P]),
         "or_decode_symbols": (ctypes.c_int64, [_P, _U64, _P]),
@@ -136,10 +141,40 @@ def single_lane_bytes(symbols: np.ndarray, freq: np.ndarray) -> int:
     return int(lib().or_single_lane_bytes(symbols.ctypes.data, symbols.size, freq.ctypes.data))
 
 
+CODEC_RANS = 0
+CODEC_HUFF = 1
+HUFF_ZERO = 0x100   # table value of a lone symbol coded in zero bits
+
+
+def huff_lengths(counts, max_len: int = 12) -> np.ndarray:
+    """Optimal code lengths of at most max_len bits (package-merge); u16 table
+    in the container's form (0 absent, HUFF_ZERO for a lone symbol)."""
+    c = np.ascontiguousarray(counts, dtype=np.uint64)
+    ln = np.zeros(256, np.uint8)
+    rc = lib().or_huff_lengths(_ptr(c), max_len, _ptr(ln))
+    if rc:
+        raise OracleError(f"or_huff_lengths: {rc}")
+    t = ln.astype(np.uint16)
+    if np.count_nonzero(c) == 1:
+        t[np.flatnonzero(c)[0]] = HUFF_ZERO
+    return t
+
+
+def huff_codes(table) -> np.ndarray:
+    """Canonical codeword of every symbol of a length table (0 if absent)."""
+    t = np.ascontiguousarray(table, dtype=np.uint16)
+    code = np.zeros(256, np.uint32)
+    if not lib().or_huff_codes(_ptr(t), _ptr(code)):
+        raise OracleError("or_huff_codes: not a complete prefix code")
+    return code
+
+
 def encode(dtype: int, rows: int, cols: int, symbols: np.ndarray, scales: np.ndarray,
            freq: np.ndarray, chunk_symbols: int = 65536, lane_run: int = 8,
-           esc_enabled: bool = False, esc_code: int = 0, esc_idx=None, esc_val=None) -> np.ndarray:
-    """Container v1 bytes (np.uint8)."""
+           esc_enabled: bool = False, esc_code: int = 0, esc_idx=None, esc_val=None,
+           codec: int = CODEC_RANS) -> np.ndarray:
+    """Container v1 bytes (np.uint8). freq is the rANS frequency table, or for
+    codec=CODEC_HUFF the code-length table."""
     symbols = np.ascontiguousarray(symbols, dtype=np.uint8)
     scales = np.ascontiguousarray(scales, dtype=np.float32)
     freq = np.ascontiguousarray(freq, dtype=np.uint16)
@@ -148,10 +183,10 @@ def encode(dtype: int, rows: int, cols: int, symbols: np.ndarray, scales: np.nda
     assert symbols.size == rows * cols and scales.size == rows and esc_idx.size == esc_val.size
     out = _P()
     n = _U64()
-    rc = lib().or_encode(dtype, rows, cols, symbols.ctypes.data, scales.ctypes.data,
-                         freq.ctypes.data, chunk_symbols, lane_run, int(esc_enabled), esc_code,
-                         esc_idx.ctypes.data, esc_val.ctypes.data, esc_idx.size,
-                         ctypes.byref(out), ctypes.byref(n))
+    rc = lib().or_encode_codec(codec, dtype, rows, cols, symbols.ctypes.data, scales.ctypes.data,
+                               freq.ctypes.data, chunk_symbols, lane_run, int(esc_enabled), esc_code,
+                               esc_idx.ctypes.data, esc_val.ctypes.data, esc_idx.size,
+                               ctypes.byref(out), ctypes.byref(n))
     if rc:
         raise OracleError(f"or_encode: {rc}")
     try:
@@ -162,13 +197,13 @@ def encode(dtype: int, rows: int, cols: int, symbols: np.ndarray, scales: np.nda
 
 
 def header(container: np.ndarray) -> dict:
-    v = np.zeros(19, dtype=np.uint64)
+    v = np.zeros(20, dtype=np.uint64)
     rc = lib().or_header_fields(container.ctypes.data, container.size, v.ctypes.data)
     if rc:
         raise OracleError(f"or_header_fields: {rc}")
     keys = ("dtype", "flags", "rows", "cols", "n", "chunk_symbols", "lane_run", "n_chunks",
             "n_esc", "esc_code", "n_words", "off_freq", "off_scales", "off_dir", "off_states",
-            "off_words", "off_esc_idx", "off_esc_val", "total")
+            "off_words", "off_esc_idx", "off_esc_val", "total", "codec")
     return {k: int(x) for k, x in zip(keys, v)}
 
 

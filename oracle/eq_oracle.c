@@ -23,9 +23,11 @@
  *          out of the entropy-optimised stream (Int8 base format).
  *  [EL] "EntroLLM: Entropy Encoded Weight Compression for Efficient Large
  *       Language Model Inference on Edge Devices", technical overview,
- *       method item 3 (parallel decoding): the coded parameter space is cut
- *       into chunks that keep the tensor structure and are decoded
- *       independently and concurrently.
+ *       method item 2 (Huffman weight encoding: frequent weight values get
+ *       short variable-length codes, rare ones long codes) and item 3
+ *       (parallel decoding): the coded parameter space is cut into chunks
+ *       that keep the tensor structure and are decoded independently and
+ *       concurrently.
  *
  * The pages fix none of the coder's bit-level choices (they only say "ANS").
  * This oracle implements "container v1", whose every choice is stated where
@@ -68,6 +70,10 @@
 #define OR_L 65536u           /* 2^16: lower bound of the coder state  */
 #define OR_HDR_BYTES 256u
 #define OR_ALIGN 256u
+#define OR_CODEC_RANS 0u      /* header offset 144: entropy coder of the stream */
+#define OR_CODEC_HUFF 1u
+#define OR_HUFF_MAXLEN 12u    /* longest Huffman codeword (bits) */
+#define OR_HUFF_ZERO 0x100u   /* table value: the only symbol, coded in zero bits */
 
 /* Status / flag values returned by the oracle. */
 #define OR_OK 0
@@ -326,6 +332,239 @@ uint64_t or_single_lane_bytes(const uint8_t *sym, uint64_t n, const uint16_t fre
 }
 
 /* ------------------------------------------------------------------------ */
+/* Huffman codec ([EL] method item 2).                                        */
+/* ------------------------------------------------------------------------ */
+/*
+ * The pages say only "Huffman coding": frequent weight values get short
+ * variable-length codes. Container v1 with codec 1 uses, as its readings:
+ *  - code lengths from the exact symbol counts, optimal among prefix codes
+ *    whose codewords have at most 12 bits (Larmore and Hirschberg's
+ *    package-merge; when no codeword of an optimal unlimited Huffman code is
+ *    longer than 12 bits the total length is the same). Coins are sorted by
+ *    (count, byte); when a coin and a package weigh the same the coin comes
+ *    first. One present symbol: length 0 ("zero-bit" code).
+ *  - canonical codewords: symbols ordered by (length, byte) get consecutive
+ *    code values, the value shifted left whenever the length grows.
+ *  - each lane's bitstream is the concatenation of its codewords, each sent
+ *    most significant bit first, packed into 16-bit words from bit 0 up
+ *    (stream bit i is bit i mod 16 of the lane's word i / 16).
+ *  - interleaving: a lane holds a bit buffer of n bits; at every step of the
+ *    chunk (same positions and lane order as the rANS codec), each active
+ *    lane with n < 12 first takes the next word of the chunk's word list
+ *    (lanes in ascending order), then every active lane decodes one codeword
+ *    from its buffer. The encoder walks the same steps to lay the words out;
+ *    a lane that runs past its bitstream takes zero words. A chunk is valid
+ *    iff every word is taken and every lane's leftover bits are zero.
+ */
+
+/* Optimal code lengths (at most L bits) for the counts: package-merge.
+ * Returns OR_OK, or OR_EINVAL if no symbol is present or 256 symbols cannot
+ * fit in L bits. len[s] = 0 for absent symbols; a lone symbol gets 0. */
+typedef struct {
+    uint64_t w;
+    int32_t leaf;      /* symbol, or -1 for a package */
+    int32_t a, b;      /* package: its two items in the previous (deeper) list */
+} or_pm_item;
+
+static void pm_count(or_pm_item *const *lists, uint32_t level, int32_t i, uint8_t len[256]) {
+    const or_pm_item *it = &lists[level][i];
+    if (it->leaf >= 0) {
+        len[it->leaf]++;
+        return;
+    }
+    pm_count(lists, level + 1, it->a, len);
+    pm_count(lists, level + 1, it->b, len);
+}
+
+int or_huff_lengths(const uint64_t counts[256], uint32_t L, uint8_t len[256]) {
+    memset(len, 0, 256);
+    uint32_t n = 0;
+    or_pm_item coins[256];
+    for (int s = 0; s < 256; s++)
+        if (counts[s]) coins[n++] = (or_pm_item){counts[s], s, -1, -1};
+    if (n == 0 || L == 0 || L > 30 || (L < 8 && n > (1u << L))) return OR_EINVAL;
+    if (n == 1) return OR_OK;
+    /* sort coins by (count, byte): insertion sort, stable on the byte order */
+    for (uint32_t i = 1; i < n; i++) {
+        or_pm_item c = coins[i];
+        uint32_t j = i;
+        while (j > 0 && coins[j - 1].w > c.w) { coins[j] = coins[j - 1]; j--; }
+        coins[j] = c;
+    }
+    /* lists[d] for depth d = 1..L; lists[L] = the coins; lists[d] = coins
+     * merged with the pairs of lists[d + 1] */
+    or_pm_item *lists[32] = {0};
+    uint32_t sizes[32] = {0};
+    for (uint32_t d = 1; d <= L; d++) {
+        lists[d] = malloc(2 * n * sizeof(or_pm_item));
+        if (!lists[d]) {
+            for (uint32_t e = 1; e <= L; e++) free(lists[e]);
+            return OR_ENOMEM;
+        }
+    }
+    memcpy(lists[L], coins, n * sizeof(or_pm_item));
+    sizes[L] = n;
+    for (uint32_t d = L - 1; d >= 1; d--) {
+        uint32_t np = sizes[d + 1] / 2, ic = 0, ip = 0, m = 0;
+        while (ic < n || ip < np) {
+            uint64_t pw = ip < np ? lists[d + 1][2 * ip].w + lists[d + 1][2 * ip + 1].w : 0;
+            if (ip >= np || (ic < n && coins[ic].w <= pw)) {
+                lists[d][m++] = coins[ic++];
+            } else {
+                lists[d][m++] = (or_pm_item){pw, -1, (int32_t)(2 * ip), (int32_t)(2 * ip + 1)};
+                ip++;
+            }
+        }
+        sizes[d] = m;
+        if (d == 1) break;
+    }
+    /* the 2n - 2 cheapest items of the top list; a symbol's length is the
+     * number of times it occurs in them */
+    for (uint32_t i = 0; i < 2 * n - 2; i++) pm_count(lists, 1, (int32_t)i, len);
+    for (uint32_t d = 1; d <= L; d++) free(lists[d]);
+    return OR_OK;
+}
+
+/* Canonical decoding tables of a length table: count[l] codewords of length
+ * l, first[l] = the code value of the first of them, sorted[] = symbols by
+ * (length, byte), offset[l] = index in sorted[] of the first of length l.
+ * Returns 1 iff the lengths form a complete prefix code (Kraft sum exactly
+ * 1), or a single zero-length symbol. */
+typedef struct {
+    uint32_t count[OR_HUFF_MAXLEN + 1], first[OR_HUFF_MAXLEN + 1], offset[OR_HUFF_MAXLEN + 1];
+    uint8_t sorted[256];
+    uint32_t nsym;
+    int zero_sym; /* the lone zero-bit symbol, or -1 */
+} or_canon;
+
+static int huff_canon(const uint16_t tab[256], or_canon *c) {
+    memset(c, 0, sizeof *c);
+    c->zero_sym = -1;
+    uint32_t nz = 0;
+    for (int s = 0; s < 256; s++) {
+        if (tab[s] == OR_HUFF_ZERO) { c->zero_sym = s; nz++; continue; }
+        if (tab[s] > OR_HUFF_MAXLEN) return 0;
+        if (tab[s]) c->count[tab[s]]++;
+    }
+    for (uint32_t l = 1; l <= OR_HUFF_MAXLEN; l++) c->nsym += c->count[l];
+    if (nz) return nz == 1 && c->nsym == 0;
+    uint64_t kraft = 0; /* in units of 2^-12 */
+    for (uint32_t l = 1; l <= OR_HUFF_MAXLEN; l++) kraft += (uint64_t)c->count[l] << (OR_HUFF_MAXLEN - l);
+    if (kraft != (1u << OR_HUFF_MAXLEN)) return 0;
+    uint32_t code = 0, off = 0;
+    for (uint32_t l = 1; l <= OR_HUFF_MAXLEN; l++) {
+        c->first[l] = code;
+        c->offset[l] = off;
+        code = (code + c->count[l]) << 1;
+        off += c->count[l];
+    }
+    uint32_t fill[OR_HUFF_MAXLEN + 1];
+    memcpy(fill, c->offset, sizeof fill);
+    for (int s = 0; s < 256; s++)
+        if (tab[s] && tab[s] != OR_HUFF_ZERO) c->sorted[fill[tab[s]]++] = (uint8_t)s;
+    return 1;
+}
+
+/* Canonical codeword of every symbol (0 for absent ones). Returns 1 on a
+ * valid table (see huff_canon). */
+int or_huff_codes(const uint16_t tab[256], uint32_t code[256]) {
+    or_canon c;
+    if (!huff_canon(tab, &c)) return 0;
+    memset(code, 0, 256 * sizeof(uint32_t));
+    for (uint32_t l = 1; l <= OR_HUFF_MAXLEN; l++)
+        for (uint32_t i = 0; i < c.count[l]; i++) code[c.sorted[c.offset[l] + i]] = c.first[l] + i;
+    return 1;
+}
+
+/* Encode one chunk with the Huffman codec: the lanes' bitstreams, then the
+ * decoder's refill schedule walked forward to order the words. words must
+ * hold nk entries (at most one word per lane-step). Returns the word count. */
+static uint64_t huff_encode_chunk(const uint8_t *sym, uint64_t nk, uint32_t K, const uint16_t tab[256],
+                                  const uint32_t code[256], uint16_t *words) {
+    uint64_t T = chunk_steps(nk, K);
+    for (int s = 0; s < 256; s++)
+        if (tab[s] == OR_HUFF_ZERO) return 0; /* a lone symbol: no bits, no words */
+    /* each lane's bitstream, one bit per byte (plain and slow) */
+    uint64_t bits_max = T * OR_HUFF_MAXLEN + 64;
+    uint8_t *bits = calloc(OR_LANES * bits_max, 1);
+    uint64_t nbits[64] = {0};
+    if (!bits) return UINT64_MAX;
+    for (uint64_t t = 0; t < T; t++) {
+        for (uint32_t j = 0; j < OR_LANES; j++) {
+            uint64_t p = lane_pos(t, j, K);
+            if (p >= nk) continue;
+            uint32_t l = tab[sym[p]] == OR_HUFF_ZERO ? 0 : tab[sym[p]];
+            for (uint32_t i = l; i-- > 0;) bits[j * bits_max + nbits[j]++] = (code[sym[p]] >> i) & 1u;
+        }
+    }
+    uint64_t nw = 0, taken[64] = {0};
+    uint32_t have[64] = {0};
+    for (uint64_t t = 0; t < T; t++) {
+        for (uint32_t j = 0; j < OR_LANES; j++) {
+            if (lane_pos(t, j, K) >= nk || have[j] >= 12) continue;
+            uint16_t w = 0;
+            for (uint32_t i = 0; i < 16; i++) {
+                uint64_t b = 16 * taken[j] + i;
+                if (b < nbits[j] && bits[j * bits_max + b]) w |= (uint16_t)(1u << i);
+            }
+            words[nw++] = w;
+            taken[j]++;
+            have[j] += 16;
+        }
+        for (uint32_t j = 0; j < OR_LANES; j++) {
+            uint64_t p = lane_pos(t, j, K);
+            if (p >= nk) continue;
+            have[j] -= tab[sym[p]] == OR_HUFF_ZERO ? 0 : tab[sym[p]];
+        }
+    }
+    free(bits);
+    return nw;
+}
+
+/* Decode one Huffman chunk: refills as above, then each active lane reads
+ * bits one at a time (least significant first), growing a code value until
+ * it names a canonical codeword of that length. Returns the flags. */
+static uint32_t huff_decode_chunk(const uint8_t *words_le, uint64_t nwords, uint64_t nk, uint32_t K,
+                                  const or_canon *c, uint8_t *sym_out) {
+    if (c->zero_sym >= 0) {
+        for (uint64_t p = 0; p < nk; p++) sym_out[p] = (uint8_t)c->zero_sym;
+        return nwords ? OR_BAD_END_STATE : 0;
+    }
+    uint32_t b[64] = {0}, n[64] = {0};
+    uint64_t ptr = 0;
+    uint64_t T = chunk_steps(nk, K);
+    for (uint64_t t = 0; t < T; t++) {
+        for (uint32_t j = 0; j < OR_LANES; j++) {
+            if (lane_pos(t, j, K) >= nk || n[j] >= 12) continue;
+            if (ptr >= nwords) return OR_WORD_OVERRUN;
+            b[j] |= (uint32_t)get_u16(words_le + 2 * ptr) << n[j];
+            n[j] += 16;
+            ptr++;
+        }
+        for (uint32_t j = 0; j < OR_LANES; j++) {
+            uint64_t p = lane_pos(t, j, K);
+            if (p >= nk) continue;
+            uint32_t v = 0, l = 0;
+            int s = -1;
+            while (s < 0) {
+                if (l == OR_HUFF_MAXLEN) return OR_BAD_END_STATE; /* not a codeword */
+                v = (v << 1) | (b[j] & 1u);
+                b[j] >>= 1;
+                n[j]--;
+                l++;
+                if (v - c->first[l] < c->count[l]) s = c->sorted[c->offset[l] + v - c->first[l]];
+            }
+            sym_out[p] = (uint8_t)s;
+        }
+    }
+    uint32_t flags = 0;
+    for (uint32_t j = 0; j < OR_LANES; j++)
+        if (b[j]) flags |= OR_BAD_END_STATE;
+    if (ptr != nwords) flags |= OR_BAD_END_STATE;
+    return flags;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Container v1 encoder.                                                     */
 /* ------------------------------------------------------------------------ */
 /*
@@ -338,7 +577,8 @@ uint64_t or_single_lane_bytes(const uint8_t *sym, uint64_t n, const uint16_t fre
  *  72 u64 n_words (all chunks, with padding)
  *  80 off_freq  88 off_scales  96 off_dir  104 off_states  112 off_words
  * 120 off_esc_idx  128 off_esc_val  136 total_bytes   (all u64 byte offsets)
- * 144..255 zero.
+ * 144 u32 codec: 0 rANS (this section's coder), 1 Huffman (further below)
+ * 148..255 zero.
  * Sections, each starting on a 256-byte boundary, gaps zero:
  *   freq[256] u16 | scales[rows] f32 | dir[n_chunks] {u64 word_start,
  *   u32 word_count, u32 0} | states[n_chunks][64] u32 | words u16 (each
@@ -348,7 +588,7 @@ uint64_t or_single_lane_bytes(const uint8_t *sym, uint64_t n, const uint16_t fre
  */
 
 typedef struct {
-    uint32_t dtype, flags, Z, K;
+    uint32_t dtype, flags, Z, K, codec;
     uint64_t rows, cols, n, n_chunks, n_esc, n_words;
     uint8_t esc_code;
     uint64_t off_freq, off_scales, off_dir, off_states, off_words, off_esc_idx, off_esc_val,
@@ -387,16 +627,19 @@ static uint64_t encode_chunk(const uint8_t *sym, uint64_t nk, uint32_t K, const 
 void or_free(void *p) { free(p); }
 
 /* Build a container v1 for one [rows, cols] tensor of byte codes.
- * freq: the table to code with (sum 4096, nonzero for every present byte).
+ * codec 0 (rANS): table = freq (sum 4096, nonzero for every present byte).
+ * codec 1 (Huffman): table = code lengths (1..12, 0 absent, 0x100 for a lone
+ *   zero-bit symbol), a complete prefix code covering every present byte.
  * esc_*: super-weight side list ([EQ] technical component 4), only with
  * esc_enabled; the stream holds esc_code exactly at the listed indices.
  * On success *out is a malloc'd buffer of *out_len bytes (free with or_free). */
-int or_encode(uint32_t dtype, uint64_t rows, uint64_t cols, const uint8_t *sym,
-              const float *scales, const uint16_t freq[256], uint32_t Z, uint32_t K,
-              uint32_t esc_enabled, uint8_t esc_code, const uint64_t *esc_idx,
-              const uint16_t *esc_val, uint64_t n_esc, uint8_t **out, uint64_t *out_len) {
+int or_encode_codec(uint32_t codec, uint32_t dtype, uint64_t rows, uint64_t cols, const uint8_t *sym,
+                    const float *scales, const uint16_t table[256], uint32_t Z, uint32_t K,
+                    uint32_t esc_enabled, uint8_t esc_code, const uint64_t *esc_idx,
+                    const uint16_t *esc_val, uint64_t n_esc, uint8_t **out, uint64_t *out_len) {
     *out = NULL;
     *out_len = 0;
+    if (codec != OR_CODEC_RANS && codec != OR_CODEC_HUFF) return OR_EINVAL;
     if (dtype != OR_DTYPE_INT8 && dtype != OR_DTYPE_E4M3) return OR_EINVAL;
     if (rows == 0 || cols == 0) return OR_EINVAL;
     if (!(K == 1 || K == 2 || K == 4 || K == 8 || K == 16)) return OR_EINVAL;
@@ -404,10 +647,12 @@ int or_encode(uint32_t dtype, uint64_t rows, uint64_t cols, const uint8_t *sym,
     if (!esc_enabled && n_esc) return OR_EINVAL;
     uint32_t cum[257];
     uint8_t s2s[4096];
-    if (!make_tables(freq, cum, s2s)) return OR_EINVAL;
+    uint32_t code[256];
+    if (codec == OR_CODEC_RANS ? !make_tables(table, cum, s2s) : !or_huff_codes(table, code))
+        return OR_EINVAL;
     uint64_t n = rows * cols;
     for (uint64_t i = 0; i < n; i++)
-        if (freq[sym[i]] == 0) return OR_EINVAL;
+        if (table[sym[i]] == 0) return OR_EINVAL;
     for (uint64_t e = 0; e < n_esc; e++) {
         if (esc_idx[e] >= n || (e > 0 && esc_idx[e] <= esc_idx[e - 1])) return OR_EINVAL;
         if (sym[esc_idx[e]] != esc_code) return OR_EINVAL;
@@ -419,7 +664,8 @@ int or_encode(uint32_t dtype, uint64_t rows, uint64_t cols, const uint8_t *sym,
     }
 
     uint64_t n_chunks = (n + Z - 1) / Z;
-    uint32_t *states = malloc(n_chunks * OR_LANES * sizeof(uint32_t));
+    uint64_t n_states = codec == OR_CODEC_RANS ? n_chunks * OR_LANES : 0;
+    uint32_t *states = malloc((n_states ? n_states : 1) * sizeof(uint32_t));
     uint64_t *wcount = malloc(n_chunks * sizeof(uint64_t));
     uint16_t *cw = malloc((n ? n : 1) * sizeof(uint16_t)); /* words of all chunks, unpadded */
     uint64_t *wstart_unpadded = malloc(n_chunks * sizeof(uint64_t));
@@ -432,7 +678,14 @@ int or_encode(uint32_t dtype, uint64_t rows, uint64_t cols, const uint8_t *sym,
         uint64_t p0 = k * Z;
         uint64_t nk = (n - p0 < Z) ? n - p0 : Z;
         wstart_unpadded[k] = used;
-        wcount[k] = encode_chunk(sym + p0, nk, K, freq, cum, states + k * OR_LANES, cw + used);
+        if (codec == OR_CODEC_RANS)
+            wcount[k] = encode_chunk(sym + p0, nk, K, table, cum, states + k * OR_LANES, cw + used);
+        else
+            wcount[k] = huff_encode_chunk(sym + p0, nk, K, table, code, cw + used);
+        if (wcount[k] == UINT64_MAX) {
+            free(states); free(wcount); free(cw); free(wstart_unpadded);
+            return OR_ENOMEM;
+        }
         used += wcount[k];
         n_words += align_up(wcount[k], 8);
     }
@@ -443,7 +696,7 @@ int or_encode(uint32_t dtype, uint64_t rows, uint64_t cols, const uint8_t *sym,
     h.off_scales = align_up(h.off_freq + 512, OR_ALIGN);
     h.off_dir = align_up(h.off_scales + rows * 4, OR_ALIGN);
     h.off_states = align_up(h.off_dir + n_chunks * 16, OR_ALIGN);
-    h.off_words = align_up(h.off_states + n_chunks * OR_LANES * 4, OR_ALIGN);
+    h.off_words = align_up(h.off_states + n_states * 4, OR_ALIGN);
     h.off_esc_idx = align_up(h.off_words + n_words * 2, OR_ALIGN);
     h.off_esc_val = align_up(h.off_esc_idx + n_esc * 8, OR_ALIGN);
     h.total = align_up(h.off_esc_val + n_esc * 2, OR_ALIGN);
@@ -463,7 +716,7 @@ int or_encode(uint32_t dtype, uint64_t rows, uint64_t cols, const uint8_t *sym,
     put_u32(buf + 32, Z);
     put_u32(buf + 36, K);
     put_u32(buf + 40, OR_LANES);
-    put_u32(buf + 44, OR_PROB_BITS);
+    put_u32(buf + 44, codec == OR_CODEC_RANS ? OR_PROB_BITS : OR_HUFF_MAXLEN);
     put_u64(buf + 48, n_chunks);
     put_u64(buf + 56, n_esc);
     buf[64] = esc_enabled ? esc_code : 0;
@@ -476,8 +729,9 @@ int or_encode(uint32_t dtype, uint64_t rows, uint64_t cols, const uint8_t *sym,
     put_u64(buf + 120, h.off_esc_idx);
     put_u64(buf + 128, h.off_esc_val);
     put_u64(buf + 136, h.total);
+    put_u32(buf + 144, codec);
 
-    for (int s = 0; s < 256; s++) put_u16(buf + h.off_freq + 2 * s, freq[s]);
+    for (int s = 0; s < 256; s++) put_u16(buf + h.off_freq + 2 * s, table[s]);
     for (uint64_t r = 0; r < rows; r++) {
         uint32_t b;
         memcpy(&b, &scales[r], 4);
@@ -490,8 +744,9 @@ int or_encode(uint32_t dtype, uint64_t rows, uint64_t cols, const uint8_t *sym,
         for (uint64_t i = 0; i < wcount[k]; i++)
             put_u16(buf + h.off_words + 2 * (wpos + i), cw[wstart_unpadded[k] + i]);
         wpos += align_up(wcount[k], 8);
-        for (uint32_t j = 0; j < OR_LANES; j++)
-            put_u32(buf + h.off_states + 4 * (k * OR_LANES + j), states[k * OR_LANES + j]);
+        if (codec == OR_CODEC_RANS)
+            for (uint32_t j = 0; j < OR_LANES; j++)
+                put_u32(buf + h.off_states + 4 * (k * OR_LANES + j), states[k * OR_LANES + j]);
     }
     for (uint64_t e = 0; e < n_esc; e++) {
         put_u64(buf + h.off_esc_idx + 8 * e, esc_idx[e]);
@@ -501,6 +756,15 @@ int or_encode(uint32_t dtype, uint64_t rows, uint64_t cols, const uint8_t *sym,
     *out = buf;
     *out_len = h.total;
     return OR_OK;
+}
+
+/* The rANS container (codec 0) with its frequency table. */
+int or_encode(uint32_t dtype, uint64_t rows, uint64_t cols, const uint8_t *sym,
+              const float *scales, const uint16_t freq[256], uint32_t Z, uint32_t K,
+              uint32_t esc_enabled, uint8_t esc_code, const uint64_t *esc_idx,
+              const uint16_t *esc_val, uint64_t n_esc, uint8_t **out, uint64_t *out_len) {
+    return or_encode_codec(OR_CODEC_RANS, dtype, rows, cols, sym, scales, freq, Z, K, esc_enabled,
+                           esc_code, esc_idx, esc_val, n_esc, out, out_len);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -529,6 +793,8 @@ static int parse(const uint8_t *b, uint64_t len, or_hdr *h) {
     h->off_esc_idx = get_u64(b + 120);
     h->off_esc_val = get_u64(b + 128);
     h->total = get_u64(b + 136);
+    h->codec = get_u32(b + 144);
+    if (h->codec != OR_CODEC_RANS && h->codec != OR_CODEC_HUFF) return OR_ECORRUPT;
     if (h->dtype != OR_DTYPE_INT8 && h->dtype != OR_DTYPE_E4M3) return OR_ECORRUPT;
     if (!(h->K == 1 || h->K == 2 || h->K == 4 || h->K == 8 || h->K == 16)) return OR_ECORRUPT;
     if (h->Z == 0 || h->Z % (OR_LANES * h->K)) return OR_ECORRUPT;
@@ -537,7 +803,7 @@ static int parse(const uint8_t *b, uint64_t len, or_hdr *h) {
     if (h->total > len) return OR_ECORRUPT;
     if (h->off_freq + 512 > h->total || h->off_scales + 4 * h->rows > h->total ||
         h->off_dir + 16 * h->n_chunks > h->total ||
-        h->off_states + 4 * OR_LANES * h->n_chunks > h->total ||
+        h->off_states + (h->codec == OR_CODEC_RANS ? 4 * OR_LANES * h->n_chunks : 0) > h->total ||
         h->off_words + 2 * h->n_words > h->total || h->off_esc_idx + 8 * h->n_esc > h->total ||
         h->off_esc_val + 2 * h->n_esc > h->total)
         return OR_ECORRUPT;
@@ -582,6 +848,7 @@ typedef struct {
     const uint16_t *freq;
     const uint32_t *cum;
     const uint8_t *s2s;
+    const or_canon *canon; /* Huffman codec */
     uint64_t k_lo, k_hi;
     uint8_t *sym_out;   /* flat, indexed by position; may be NULL */
     uint16_t *bf16_out; /* flat, indexed by position; may be NULL */
@@ -604,8 +871,11 @@ static uint32_t decode_range(or_job *jb) {
         uint64_t wc = get_u32(b + h->off_dir + 16 * k + 8);
         if (ws + wc > h->n_words) { flags |= OR_WORD_OVERRUN; continue; }
         uint8_t *dst = jb->sym_out ? jb->sym_out + p0 : tmp;
-        flags |= decode_chunk(b + h->off_words + 2 * ws, wc, b + h->off_states + 4 * OR_LANES * k,
-                              nk, h->K, jb->freq, jb->cum, jb->s2s, dst);
+        if (h->codec == OR_CODEC_RANS)
+            flags |= decode_chunk(b + h->off_words + 2 * ws, wc, b + h->off_states + 4 * OR_LANES * k,
+                                  nk, h->K, jb->freq, jb->cum, jb->s2s, dst);
+        else
+            flags |= huff_decode_chunk(b + h->off_words + 2 * ws, wc, nk, h->K, jb->canon, dst);
         if (jb->bf16_out) {
             for (uint64_t i = 0; i < nk; i++) {
                 uint64_t pos = p0 + i;
@@ -646,7 +916,9 @@ int64_t or_decode_chunks(const uint8_t *buf, uint64_t len, uint64_t k_lo, uint64
     for (int s = 0; s < 256; s++) freq[s] = get_u16(buf + h.off_freq + 2 * s);
     uint32_t cum[257];
     uint8_t s2s[4096];
-    if (!make_tables(freq, cum, s2s)) return OR_ECORRUPT;
+    or_canon canon;
+    if (h.codec == OR_CODEC_RANS ? !make_tables(freq, cum, s2s) : !huff_canon(freq, &canon))
+        return OR_ECORRUPT;
     if (nthreads < 1) nthreads = 1;
     uint64_t nk = k_hi - k_lo;
     if (nthreads > nk) nthreads = nk ? (uint32_t)nk : 1;
@@ -654,7 +926,7 @@ int64_t or_decode_chunks(const uint8_t *buf, uint64_t len, uint64_t k_lo, uint64
     pthread_t *tid = calloc(nthreads, sizeof(pthread_t));
     if (!jobs || !tid) { free(jobs); free(tid); return OR_ENOMEM; }
     for (uint32_t i = 0; i < nthreads; i++) {
-        jobs[i] = (or_job){buf, &h, freq, cum, s2s, k_lo + nk * i / nthreads,
+        jobs[i] = (or_job){buf, &h, freq, cum, s2s, &canon, k_lo + nk * i / nthreads,
                            k_lo + nk * (i + 1) / nthreads, sym_out, bf16_out, 0};
     }
     for (uint32_t i = 1; i < nthreads; i++) pthread_create(&tid[i], NULL, decode_thread, &jobs[i]);
@@ -679,14 +951,14 @@ int64_t or_decode_dequant(const uint8_t *buf, uint64_t len, uint16_t *bf16_out) 
 
 /* Header fields for the Python side: fills v[0..16) with dtype, flags, rows,
  * cols, n, Z, K, n_chunks, n_esc, esc_code, n_words, off_freq, off_scales,
- * off_dir, off_states, off_words; v[16..19) = off_esc_idx, off_esc_val, total. */
-int or_header_fields(const uint8_t *buf, uint64_t len, uint64_t v[19]) {
+ * off_dir, off_states, off_words; v[16..20) = off_esc_idx, off_esc_val, total, codec. */
+int or_header_fields(const uint8_t *buf, uint64_t len, uint64_t v[20]) {
     or_hdr h;
     int st = parse(buf, len, &h);
     if (st) return st;
-    uint64_t f[19] = {h.dtype, h.flags, h.rows, h.cols, h.n, h.Z, h.K, h.n_chunks, h.n_esc,
+    uint64_t f[20] = {h.dtype, h.flags, h.rows, h.cols, h.n, h.Z, h.K, h.n_chunks, h.n_esc,
                       h.esc_code, h.n_words, h.off_freq, h.off_scales, h.off_dir, h.off_states,
-                      h.off_words, h.off_esc_idx, h.off_esc_val, h.total};
+                      h.off_words, h.off_esc_idx, h.off_esc_val, h.total, h.codec};
     memcpy(v, f, sizeof f);
     return OR_OK;
 }

@@ -16,6 +16,10 @@ constexpr uint64_t kSectionAlign = 256;
 constexpr uint32_t kWordPad = 8;                  // words per chunk padded to a multiple of 8
 constexpr uint32_t kMaxChunk = 1u << 24;
 constexpr uint64_t kDirEntryBytes = 16;
+constexpr uint32_t kCodecRans = 0;
+constexpr uint32_t kCodecHuffman = 1;
+constexpr uint32_t kHuffMaxLen = 12;        // longest codeword
+constexpr uint16_t kHuffZero = 0x100;       // length-table value of a lone zero-bit symbol
 
 // Header byte offsets.
 enum HeaderField : uint32_t {
@@ -23,6 +27,7 @@ enum HeaderField : uint32_t {
     H_CHUNK = 32, H_LANE_RUN = 36, H_LANES = 40, H_PROB_BITS = 44, H_NCHUNKS = 48, H_NESC = 56,
     H_ESC_CODE = 64, H_NWORDS = 72, H_OFF_FREQ = 80, H_OFF_SCALES = 88, H_OFF_DIR = 96,
     H_OFF_STATES = 104, H_OFF_WORDS = 112, H_OFF_ESC_IDX = 120, H_OFF_ESC_VAL = 128, H_TOTAL = 136,
+    H_CODEC = 144,
 };
 
 constexpr uint64_t round_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
@@ -32,8 +37,10 @@ struct Sections {
 };
 
 // Section offsets of a container with the given counts: each section starts
-// on a 256-byte boundary right after the previous one.
-inline Sections layout(uint64_t rows, uint64_t n_chunks, uint64_t n_words, uint64_t n_esc) {
+// on a 256-byte boundary right after the previous one (the Huffman codec
+// stores no lane states).
+inline Sections layout(uint64_t rows, uint64_t n_chunks, uint64_t n_words, uint64_t n_esc,
+                       uint32_t codec = kCodecRans) {
     Sections s{};
     uint64_t at = kHeaderBytes;
     auto place = [&](uint64_t bytes) {
@@ -44,7 +51,7 @@ inline Sections layout(uint64_t rows, uint64_t n_chunks, uint64_t n_words, uint6
     s.freq = place(256 * 2);
     s.scales = place(rows * 4);
     s.dir = place(n_chunks * kDirEntryBytes);
-    s.states = place(n_chunks * kLanes * 4);
+    s.states = place(codec == kCodecRans ? n_chunks * kLanes * 4 : 0);
     s.words = place(n_words * 2);
     s.esc_idx = place(n_esc * 8);
     s.esc_val = place(n_esc * 2);

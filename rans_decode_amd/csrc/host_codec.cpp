@@ -148,6 +148,147 @@ uint64_t encode_chunk(const uint8_t *sym, uint32_t nk, uint32_t K, const SymInfo
 
 bool is_e4m3_nan(uint8_t c) { return (c & 0x7Fu) == 0x7Fu; }
 
+// ---------------------------------------------------------------------------
+// Huffman codec (EntroLLM technical overview, method item 2).
+// ---------------------------------------------------------------------------
+
+// Code lengths of at most kHuffMaxLen bits minimising sum count * length
+// (package-merge). Items of one list are kept sorted by weight; a package of
+// the deeper list is placed after coins of the same weight. Coins are the
+// present symbols in (count, byte) order. Returns false if none is present.
+// A lone present symbol gets kHuffZero.
+bool huffman_lengths(const uint64_t counts[256], uint16_t table[256]) {
+    struct Node { uint64_t weight; int32_t sym; uint32_t left; };  // package: children left, left + 1
+    std::vector<uint32_t> present;
+    for (uint32_t c = 0; c < 256; ++c)
+        if (counts[c]) present.push_back(c);
+    std::fill(table, table + 256, 0);
+    if (present.empty()) return false;
+    if (present.size() == 1) {
+        table[present[0]] = kHuffZero;
+        return true;
+    }
+    std::stable_sort(present.begin(), present.end(),
+                     [&](uint32_t a, uint32_t b) { return counts[a] < counts[b]; });
+    const size_t n = present.size();
+    // level[L - 1] is the deepest list; level[0] the top one
+    std::vector<std::vector<Node>> level(kHuffMaxLen);
+    for (uint32_t d = kHuffMaxLen; d-- > 0;) {
+        std::vector<Node> &cur = level[d];
+        const std::vector<Node> *deeper = d + 1 < kHuffMaxLen ? &level[d + 1] : nullptr;
+        const size_t packs = deeper ? deeper->size() / 2 : 0;
+        cur.reserve(n + packs);
+        size_t c = 0, q = 0;
+        while (c < n || q < packs) {
+            const uint64_t pw = q < packs ? (*deeper)[2 * q].weight + (*deeper)[2 * q + 1].weight : 0;
+            if (q == packs || (c < n && counts[present[c]] <= pw)) {
+                cur.push_back({counts[present[c]], (int32_t)present[c], 0});
+                ++c;
+            } else {
+                cur.push_back({pw, -1, (uint32_t)(2 * q)});
+                ++q;
+            }
+        }
+    }
+    // each symbol's length = its occurrences in the 2n - 2 cheapest top items
+    std::vector<std::pair<uint32_t, uint32_t>> stack;  // (depth, index)
+    for (uint32_t i = 0; i < 2 * n - 2; ++i) stack.push_back({0, i});
+    while (!stack.empty()) {
+        const auto [d, i] = stack.back();
+        stack.pop_back();
+        const Node &nd = level[d][i];
+        if (nd.sym >= 0) {
+            ++table[nd.sym];
+        } else {
+            stack.push_back({d + 1, nd.left});
+            stack.push_back({d + 1, nd.left + 1});
+        }
+    }
+    return true;
+}
+
+// Canonical codewords of a complete length table: (length, byte) order,
+// consecutive values, shifted left when the length grows.
+void huffman_codes(const uint16_t table[256], uint32_t code[256]) {
+    uint32_t count[kHuffMaxLen + 2] = {};
+    for (int s = 0; s < 256; ++s)
+        if (table[s] && table[s] <= kHuffMaxLen) ++count[table[s]];
+    uint32_t next[kHuffMaxLen + 2] = {};
+    uint32_t c = 0;
+    for (uint32_t l = 1; l <= kHuffMaxLen; ++l) {
+        next[l] = c;
+        c = (c + count[l]) << 1;
+    }
+    for (int s = 0; s < 256; ++s) code[s] = (table[s] && table[s] <= kHuffMaxLen) ? next[table[s]]++ : 0;
+}
+
+// True iff the table is a complete prefix code of lengths 1..12, or exactly
+// one kHuffZero entry and nothing else; sets *lone to that symbol or -1.
+bool huffman_table_ok(const uint16_t table[256], int32_t *lone) {
+    uint64_t kraft = 0;
+    int zeros = 0, coded = 0;
+    *lone = -1;
+    for (int s = 0; s < 256; ++s) {
+        const uint16_t l = table[s];
+        if (l == kHuffZero) { ++zeros; *lone = s; continue; }
+        if (l > kHuffMaxLen) return false;
+        if (l) { ++coded; kraft += 1ull << (kHuffMaxLen - l); }
+    }
+    if (zeros) return zeros == 1 && coded == 0;
+    return kraft == (1ull << kHuffMaxLen);
+}
+
+// Huffman-codes one chunk: each lane's codewords go into its own 16-bit word
+// list (most significant codeword bit first, from bit 0 of a word up); then
+// the decoder's step loop is replayed to interleave those lists: at each
+// step an active lane holding fewer than 12 bits takes its next word (zero
+// once its list is used up). `out` has room for nk words. Returns the count.
+uint64_t huffman_encode_chunk(const uint8_t *sym, uint32_t nk, uint32_t K, const uint16_t table[256],
+                              const uint32_t code[256], uint16_t *out) {
+    for (int s = 0; s < 256; ++s)
+        if (table[s] == kHuffZero) return 0;  // a lone zero-bit symbol: no words
+    const uint32_t group = kLanes * K;
+    const uint32_t steps = (nk + group - 1) / group * K;
+    auto pos_of = [&](uint32_t t, uint32_t j) { return (t / K) * group + j * K + (t % K); };
+    std::vector<std::vector<uint16_t>> lane_words(kLanes);
+    for (uint32_t j = 0; j < kLanes; ++j) {
+        uint64_t acc = 0;
+        uint32_t bits = 0;
+        std::vector<uint16_t> &w = lane_words[j];
+        for (uint32_t t = 0; t < steps; ++t) {
+            const uint32_t p = pos_of(t, j);
+            if (p >= nk) break;  // a lane's positions only grow with t
+            const uint32_t l = table[sym[p]];
+            const uint32_t c = code[sym[p]];
+            for (uint32_t i = 0; i < l; ++i)  // codeword MSB first into rising bit positions
+                acc |= (uint64_t)((c >> (l - 1 - i)) & 1u) << (bits + i);
+            bits += l;
+            while (bits >= 16) {
+                w.push_back((uint16_t)acc);
+                acc >>= 16;
+                bits -= 16;
+            }
+        }
+        if (bits) w.push_back((uint16_t)acc);
+    }
+    uint32_t held[kLanes] = {};
+    size_t next[kLanes] = {};
+    uint64_t nw = 0;
+    for (uint32_t t = 0; t < steps; ++t) {
+        for (uint32_t j = 0; j < kLanes; ++j) {
+            const uint32_t p = pos_of(t, j);
+            if (p >= nk) continue;
+            if (held[j] < 12) {
+                out[nw++] = next[j] < lane_words[j].size() ? lane_words[j][next[j]] : 0;
+                ++next[j];
+                held[j] += 16;
+            }
+            held[j] -= table[sym[p]];
+        }
+    }
+    return nw;
+}
+
 }  // namespace
 
 extern "C" {
@@ -199,9 +340,21 @@ eq_status eq_encode_host(const eq_tables *t, const eq_tensor_desc *d, const uint
     if (Z == 0 || Z > kMaxChunk || Z % (kLanes * K) != 0) return EQ_EINVAL;
     if (!d->esc_enabled && n_esc) return EQ_EINVAL;
     if (d->esc_enabled && d->esc_code > 255) return EQ_EINVAL;
-    uint32_t fsum = 0;
-    for (int s = 0; s < 256; ++s) fsum += t->freq[s];
-    if (fsum != kProbScale) return EQ_EINVAL;
+    if (d->codec != kCodecRans && d->codec != kCodecHuffman) return EQ_EINVAL;
+    const bool huff = d->codec == kCodecHuffman;
+    // the per-symbol table the container stores: rANS frequencies, or
+    // Huffman code lengths derived from the counts
+    uint16_t table[256];
+    if (huff) {
+        if (!huffman_lengths(t->counts, table)) return EQ_EINVAL;
+    } else {
+        uint32_t fsum = 0;
+        for (int s = 0; s < 256; ++s) {
+            fsum += t->freq[s];
+            table[s] = t->freq[s];
+        }
+        if (fsum != kProbScale) return EQ_EINVAL;
+    }
 
     const uint64_t n = d->rows * d->cols;
     for (uint64_t r = 0; r < d->rows; ++r)
@@ -222,7 +375,7 @@ eq_status eq_encode_host(const eq_tables *t, const eq_tensor_desc *d, const uint
         bool b = false;
         for (uint64_t k = lo; k < hi; ++k) {
             const uint8_t c = symbols[k];
-            b |= t->freq[c] == 0;
+            b |= table[c] == 0;
             const bool is_esc = d->esc_enabled && c == d->esc_code;
             seen += is_esc;
             b |= d->dtype == EQ_DTYPE_E4M3 && is_e4m3_nan(c) && !is_esc;
@@ -238,13 +391,16 @@ eq_status eq_encode_host(const eq_tables *t, const eq_tensor_desc *d, const uint
     if (esc_total != n_esc) return EQ_EINVAL;
 
     SymInfo tab[256];
-    for (int s = 0; s < 256; ++s) {
-        tab[s].freq = t->freq[s] ? t->freq[s] : 1;
-        tab[s].start = t->cum[s];
-        tab[s].renorm_at = (uint64_t)t->freq[s] << 20;
-    }
-    {   // cum must match freq
-        uint32_t c = 0;
+    uint32_t hcode[256];
+    if (huff) {
+        huffman_codes(table, hcode);
+    } else {
+        for (int s = 0; s < 256; ++s) {
+            tab[s].freq = t->freq[s] ? t->freq[s] : 1;
+            tab[s].start = t->cum[s];
+            tab[s].renorm_at = (uint64_t)t->freq[s] << 20;
+        }
+        uint32_t c = 0;  // cum must match freq
         for (int s = 0; s < 256; ++s) {
             if (t->cum[s] != c) return EQ_EINVAL;
             c += t->freq[s];
@@ -253,21 +409,25 @@ eq_status eq_encode_host(const eq_tables *t, const eq_tensor_desc *d, const uint
 
     const uint64_t n_chunks = (n + Z - 1) / Z;
     std::unique_ptr<uint16_t[]> scratch(new (std::nothrow) uint16_t[n]);
-    std::unique_ptr<uint32_t[]> states(new (std::nothrow) uint32_t[n_chunks * kLanes]);
+    std::unique_ptr<uint32_t[]> states(new (std::nothrow) uint32_t[huff ? 1 : n_chunks * kLanes]);
     std::unique_ptr<uint64_t[]> wcount(new (std::nothrow) uint64_t[n_chunks]);
     if (!scratch || !states || !wcount) return EQ_ENOMEM;
 
-    // chunk k encodes into scratch[k*Z, k*Z + nk), filled from its end
+    // chunk k encodes into scratch[k*Z, k*Z + nk): rANS fills it from its
+    // end, Huffman from its start
     parallel_for(n_chunks, [&](uint64_t k) {
         const uint64_t p0 = k * Z;
         const uint32_t nk = (uint32_t)std::min<uint64_t>(Z, n - p0);
-        wcount[k] = encode_chunk(symbols + p0, nk, K, tab, &states[k * kLanes],
-                                 scratch.get() + p0 + nk);
+        if (huff)
+            wcount[k] = huffman_encode_chunk(symbols + p0, nk, K, table, hcode, scratch.get() + p0);
+        else
+            wcount[k] = encode_chunk(symbols + p0, nk, K, tab, &states[k * kLanes],
+                                     scratch.get() + p0 + nk);
     });
 
     uint64_t n_words = 0;
     for (uint64_t k = 0; k < n_chunks; ++k) n_words += round_up(wcount[k], kWordPad);
-    const Sections sec = layout(d->rows, n_chunks, n_words, n_esc);
+    const Sections sec = layout(d->rows, n_chunks, n_words, n_esc, d->codec);
     *out_len = sec.total;
     if (!out || cap < sec.total) return EQ_ERANGE;
 
@@ -283,7 +443,7 @@ eq_status eq_encode_host(const eq_tables *t, const eq_tensor_desc *d, const uint
     wr32(b + H_CHUNK, Z);
     wr32(b + H_LANE_RUN, K);
     wr32(b + H_LANES, kLanes);
-    wr32(b + H_PROB_BITS, kProbBits);
+    wr32(b + H_PROB_BITS, huff ? kHuffMaxLen : kProbBits);
     wr64(b + H_NCHUNKS, n_chunks);
     wr64(b + H_NESC, n_esc);
     b[H_ESC_CODE] = d->esc_enabled ? (uint8_t)d->esc_code : 0;
@@ -295,8 +455,10 @@ eq_status eq_encode_host(const eq_tables *t, const eq_tensor_desc *d, const uint
     auto zero_to = [&](uint64_t from, uint64_t to) {
         if (to > from) std::memset(b + from, 0, to - from);
     };
+    zero_to(H_CODEC, sec.freq);
+    wr32(b + H_CODEC, d->codec);
     zero_to(sec.freq, sec.total);  // gaps and padding words are zero
-    for (int s = 0; s < 256; ++s) wr16(b + sec.freq + 2 * s, t->freq[s]);
+    for (int s = 0; s < 256; ++s) wr16(b + sec.freq + 2 * s, table[s]);
     std::memcpy(b + sec.scales, scales, d->rows * 4);
 
     std::vector<uint64_t> first(n_chunks);
@@ -306,11 +468,11 @@ eq_status eq_encode_host(const eq_tables *t, const eq_tensor_desc *d, const uint
         wr64(b + sec.dir + kDirEntryBytes * k, first[k]);
         wr32(b + sec.dir + kDirEntryBytes * k + 8, (uint32_t)wcount[k]);
     }
-    std::memcpy(b + sec.states, states.get(), n_chunks * kLanes * 4);
+    if (!huff) std::memcpy(b + sec.states, states.get(), n_chunks * kLanes * 4);
     parallel_for(n_chunks, [&](uint64_t k) {
         const uint64_t p0 = k * Z;
         const uint64_t nk = std::min<uint64_t>(Z, n - p0);
-        const uint16_t *src = scratch.get() + p0 + nk - wcount[k];
+        const uint16_t *src = huff ? scratch.get() + p0 : scratch.get() + p0 + nk - wcount[k];
         std::memcpy(b + sec.words + 2 * first[k], src, 2 * wcount[k]);
     });
     for (uint64_t e = 0; e < n_esc; ++e) {
@@ -346,10 +508,15 @@ eq_status eq_parse_header(const void *bytes, uint64_t len, eq_header *out) {
     h.off_esc_val = rd64(b + H_OFF_ESC_VAL);
     h.total_bytes = rd64(b + H_TOTAL);
     h.single_symbol = -1;
+    h.codec = rd32(b + H_CODEC);
+    h.reserved = 0;
+    if (h.codec != kCodecRans && h.codec != kCodecHuffman) return EQ_ECORRUPT;
+    const bool huff = h.codec == kCodecHuffman;
 
     if (h.dtype != EQ_DTYPE_INT8 && h.dtype != EQ_DTYPE_E4M3) return EQ_ECORRUPT;
     if (h.flags > 1 || (!(h.flags & 1) && (h.n_esc || h.esc_code))) return EQ_ECORRUPT;
-    if (rd32(b + H_LANES) != kLanes || rd32(b + H_PROB_BITS) != kProbBits) return EQ_ECORRUPT;
+    if (rd32(b + H_LANES) != kLanes || rd32(b + H_PROB_BITS) != (huff ? kHuffMaxLen : kProbBits))
+        return EQ_ECORRUPT;
     if (!valid_lane_run(h.lane_run)) return EQ_ECORRUPT;
     if (h.chunk_symbols == 0 || h.chunk_symbols > kMaxChunk ||
         h.chunk_symbols % (kLanes * h.lane_run))
@@ -360,22 +527,30 @@ eq_status eq_parse_header(const void *bytes, uint64_t len, eq_header *out) {
     if (h.n_esc > h.n || h.n_words > h.n + 8 * h.n_chunks) return EQ_ECORRUPT;
     for (size_t i = 65; i < 72; ++i)
         if (b[i]) return EQ_ECORRUPT;
-    for (size_t i = 144; i < kHeaderBytes; ++i)
+    for (size_t i = H_CODEC + 4; i < kHeaderBytes; ++i)
         if (b[i]) return EQ_ECORRUPT;
-    const Sections sec = layout(h.rows, h.n_chunks, h.n_words, h.n_esc);
+    const Sections sec = layout(h.rows, h.n_chunks, h.n_words, h.n_esc, h.codec);
     if (h.off_freq != sec.freq || h.off_scales != sec.scales || h.off_dir != sec.dir ||
         h.off_states != sec.states || h.off_words != sec.words || h.off_esc_idx != sec.esc_idx ||
         h.off_esc_val != sec.esc_val || h.total_bytes != sec.total)
         return EQ_ECORRUPT;
     if (len < h.total_bytes) return EQ_ECORRUPT;
 
-    uint32_t fsum = 0;
-    for (int s = 0; s < 256; ++s) {
-        const uint16_t f = rd16(b + h.off_freq + 2 * s);
-        fsum += f;
-        if (f == kProbScale) h.single_symbol = s;
+    if (huff) {
+        uint16_t table[256];
+        for (int s = 0; s < 256; ++s) table[s] = rd16(b + h.off_freq + 2 * s);
+        int32_t lone;
+        if (!huffman_table_ok(table, &lone)) return EQ_ECORRUPT;
+        h.single_symbol = lone;
+    } else {
+        uint32_t fsum = 0;
+        for (int s = 0; s < 256; ++s) {
+            const uint16_t f = rd16(b + h.off_freq + 2 * s);
+            fsum += f;
+            if (f == kProbScale) h.single_symbol = s;
+        }
+        if (fsum != kProbScale) return EQ_ECORRUPT;
     }
-    if (fsum != kProbScale) return EQ_ECORRUPT;
 
     // directory: consecutive padded word ranges covering exactly n_words
     uint64_t at = 0;
@@ -389,8 +564,9 @@ eq_status eq_parse_header(const void *bytes, uint64_t len, eq_header *out) {
     }
     if (at != h.n_words) return EQ_ECORRUPT;
     // lane states: a valid encoder end state lies in [2^16, 2^32)
-    for (uint64_t i = 0; i < h.n_chunks * kLanes; ++i)
-        if (rd32(b + h.off_states + 4 * i) < kStateLow) return EQ_ECORRUPT;
+    if (!huff)
+        for (uint64_t i = 0; i < h.n_chunks * kLanes; ++i)
+            if (rd32(b + h.off_states + 4 * i) < kStateLow) return EQ_ECORRUPT;
     for (uint64_t e = 0; e < h.n_esc; ++e) {
         const uint64_t idx = rd64(b + h.off_esc_idx + 8 * e);
         if (idx >= h.n || (e && idx <= rd64(b + h.off_esc_idx + 8 * (e - 1)))) return EQ_ECORRUPT;

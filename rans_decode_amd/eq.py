@@ -28,6 +28,8 @@ EQ_OK, EQ_EINVAL, EQ_ERANGE, EQ_ECORRUPT, EQ_EHIP, EQ_EUNSUPPORTED, EQ_ENOMEM = 
 EQ_DEV_BAD_END_STATE, EQ_DEV_WORD_OVERRUN = 1, 2
 EQ_DTYPE_INT8, EQ_DTYPE_E4M3 = 1, 2
 EQ_MAX_BLOCK_TENSORS = 16
+EQ_CODEC_RANS = 0
+EQ_CODEC_HUFFMAN = 1
 
 _u32, _u64, _i32, _vp = ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int32, ctypes.c_void_p
 
@@ -40,14 +42,14 @@ class eq_tables(ctypes.Structure):
 class eq_tensor_desc(ctypes.Structure):
     _fields_ = [("dtype", _u32), ("lane_run", _u32), ("rows", _u64), ("cols", _u64),
                 ("chunk_symbols", _u32), ("esc_enabled", _u32), ("esc_code", _u32),
-                ("reserved", _u32)]
+                ("codec", _u32)]
 
 
 class eq_header(ctypes.Structure):
     _fields_ = [("dtype", _u32), ("flags", _u32), ("chunk_symbols", _u32), ("lane_run", _u32),
                 ("rows", _u64), ("cols", _u64), ("n", _u64), ("n_chunks", _u64), ("n_esc", _u64),
                 ("n_words", _u64), ("esc_code", _u32), ("single_symbol", _i32),
-                ("off_freq", _u64), ("off_scales", _u64), ("off_dir", _u64), ("off_states", _u64),
+                ("codec", _u32), ("reserved", _u32), ("off_freq", _u64), ("off_scales", _u64), ("off_dir", _u64), ("off_states", _u64),
                 ("off_words", _u64), ("off_esc_idx", _u64), ("off_esc_val", _u64),
                 ("total_bytes", _u64)]
 
@@ -168,11 +170,11 @@ def eq_encode_host(tables: eq_tables, desc: eq_tensor_desc, symbols: np.ndarray,
 
 def encode_host(tables: eq_tables, dtype: int, rows: int, cols: int, symbols: np.ndarray,
                 scales: np.ndarray, esc_idx=None, esc_val=None, esc_code: int = 0,
-                chunk_symbols: int = 65536, lane_run: int = 8) -> np.ndarray:
+                chunk_symbols: int = 65536, lane_run: int = 8, codec: int = 0) -> np.ndarray:
     n_esc = 0 if esc_idx is None else len(esc_idx)
     d = eq_tensor_desc(dtype=dtype, lane_run=lane_run, rows=rows, cols=cols,
                        chunk_symbols=chunk_symbols, esc_enabled=1 if n_esc or esc_code else 0,
-                       esc_code=esc_code, reserved=0)
+                       esc_code=esc_code, codec=codec)
     return eq_encode_host(tables, d, symbols, scales, esc_idx, esc_val)
 
 

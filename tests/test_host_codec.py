@@ -19,12 +19,23 @@ def test_library_exports_every_declared_function():
         assert hasattr(lib, n), n
 
 
-def test_struct_sizes_match_c_layout():
-    assert ctypes.sizeof(eq.eq_tables) == 3600
-    assert ctypes.sizeof(eq.eq_tensor_desc) == 40
-    assert ctypes.sizeof(eq.eq_header) == 136
-    assert ctypes.sizeof(eq.eq_tensor_ref) == 152
-    assert ctypes.sizeof(eq.eq_block) == 24
+def test_struct_sizes_match_c_layout(tmp_path):
+    """The binding's ctypes structs against the C compiler's view of eq.h."""
+    import os
+    import subprocess
+    src = tmp_path / "sizes.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "eq.h"\n'
+                   'int main(void) { printf("%zu %zu %zu %zu %zu %zu %zu\\n", sizeof(eq_tables),'
+                   ' sizeof(eq_tensor_desc), sizeof(eq_header), sizeof(eq_tensor_ref), sizeof(eq_block),'
+                   ' offsetof(eq_header, codec), offsetof(eq_header, off_freq)); return 0; }\n')
+    exe = tmp_path / "sizes"
+    inc = os.path.join(os.path.dirname(eq.HEADER_PATH))
+    subprocess.check_call(["gcc", "-std=c11", "-I", inc, str(src), "-o", str(exe)])
+    got = [int(v) for v in subprocess.check_output([str(exe)]).split()]
+    assert got == [ctypes.sizeof(eq.eq_tables), ctypes.sizeof(eq.eq_tensor_desc),
+                   ctypes.sizeof(eq.eq_header), ctypes.sizeof(eq.eq_tensor_ref),
+                   ctypes.sizeof(eq.eq_block), eq.eq_header.codec.offset,
+                   eq.eq_header.off_freq.offset]
 
 
 def test_status_strings():
@@ -235,3 +246,90 @@ def test_encode_size_query():
     assert st == eq.EQ_ERANGE
     c = eq.eq_encode_host(tab, d, sym, sc)
     assert c.size == need.value
+
+
+# --- Huffman codec (EntroLLM method item 2): the library's encoder against the oracle's
+
+def test_huffman_encode_byte_equal_random_layouts():
+    """Code lengths (package-merge), canonical codes, bit packing and the
+    interleaved word order: byte-equal containers on random layouts."""
+    rng = np.random.default_rng(23)
+    for it in range(300):
+        K = int(rng.choice([1, 2, 4, 8, 16]))
+        Z = 64 * K * int(rng.integers(1, 6))
+        n = int(rng.integers(1, 4 * Z + 1))
+        k = int(rng.integers(1, 40))
+        present = rng.choice(256, size=k, replace=False)
+        w = rng.exponential(1.0, k) ** 3 + 1e-4
+        sym = present[rng.choice(k, size=n, p=w / w.sum())].astype(np.uint8)
+        divs = [d for d in range(1, n + 1) if n % d == 0]
+        rows = int(rng.choice(divs))
+        cols = n // rows
+        scales = rng.uniform(-1, 1, rows).astype(np.float32)
+        tab = eq.build_tables(sym)
+        ours = eq.encode_host(tab, 1, rows, cols, sym, scales, chunk_symbols=Z, lane_run=K,
+                              codec=eq.EQ_CODEC_HUFFMAN)
+        lens = oracle.huff_lengths(np.array(tab.counts, np.uint64))
+        ref = oracle.encode(1, rows, cols, sym, scales, lens, Z, K, codec=oracle.CODEC_HUFF)
+        assert np.array_equal(ours, ref), (it, K, Z, n)
+        h = eq.parse_header(ours)
+        assert h.codec == eq.EQ_CODEC_HUFFMAN
+        distinct = sorted(set(sym.tolist()))
+        assert h.single_symbol == (distinct[0] if len(distinct) == 1 else -1)
+
+
+def test_huffman_encode_byte_equal_configs_and_escapes():
+    for cfg, spec in [(1, None), (4, synth.TensorSpec("down", 48, 4096, synth.DTYPE_INT8, 2.1, 4)),
+                      (3, synth.TensorSpec("q", 64, 4096, synth.DTYPE_E4M3, 2.1, 3))]:
+        t = synth.make_tensor(cfg, 0, 6 if spec and spec.n_esc else 0, spec=spec)
+        sp = t.spec
+        tab = eq.build_tables(t.symbols)
+        esc = t.esc_idx.size > 0
+        ours = eq.encode_host(tab, sp.dtype, sp.rows, sp.cols, t.symbols, t.scales,
+                              t.esc_idx if esc else None, t.esc_val if esc else None,
+                              esc_code=t.esc_code if esc else 0, codec=eq.EQ_CODEC_HUFFMAN)
+        lens = oracle.huff_lengths(np.array(tab.counts, np.uint64))
+        ref = oracle.encode(sp.dtype, sp.rows, sp.cols, t.symbols, t.scales, lens,
+                            esc_enabled=esc, esc_code=t.esc_code if esc else 0,
+                            esc_idx=t.esc_idx if esc else None, esc_val=t.esc_val if esc else None,
+                            codec=oracle.CODEC_HUFF)
+        assert np.array_equal(ours, ref), cfg
+        d, fl = oracle.decode_symbols(ours)
+        assert fl == 0 and np.array_equal(d, t.symbols)
+
+
+def test_huffman_lone_symbol_and_parse_checks():
+    sym = np.full(5000, 0x07, np.uint8)
+    c = eq.encode_host(eq.build_tables(sym), 1, 50, 100, sym, np.ones(50, np.float32),
+                       codec=eq.EQ_CODEC_HUFFMAN)
+    h = eq.parse_header(c)
+    assert h.single_symbol == 7 and h.n_words == 0 and h.codec == eq.EQ_CODEC_HUFFMAN
+    # no lane-state section: words start where the states would
+    assert h.off_states == h.off_words
+    rng = np.random.default_rng(3)
+    sym = rng.choice([1, 2, 3, 200], 9000, p=[0.7, 0.2, 0.07, 0.03]).astype(np.uint8)
+    c = eq.encode_host(eq.build_tables(sym), 1, 9, 1000, sym, np.ones(9, np.float32),
+                       codec=eq.EQ_CODEC_HUFFMAN)
+    h = eq.parse_header(c)
+    lens = c[h.off_freq:h.off_freq + 512].view(np.uint16)
+    for name, mutate in [("kraft", lambda t: t.__setitem__(1, t[1] + 1)),
+                         ("too long", lambda t: t.__setitem__(2, 13)),
+                         ("zero-bit with others", lambda t: t.__setitem__(3, 0x100)),
+                         ("codec", None)]:
+        bad = c.copy()
+        if mutate is None:
+            bad[144] = 7
+        else:
+            t = lens.copy()
+            mutate(t)
+            bad[h.off_freq:h.off_freq + 512] = t.view(np.uint8)
+        with pytest.raises(eq.EqError) as ei:
+            eq.parse_header(bad)
+        assert ei.value.status == eq.EQ_ECORRUPT, name
+    # a present symbol without a count cannot get a codeword
+    tab = eq.build_tables(sym)
+    tab.counts[200] = 0
+    with pytest.raises(eq.EqError):
+        eq.encode_host(tab, 1, 9, 1000, sym, np.ones(9, np.float32), codec=eq.EQ_CODEC_HUFFMAN)
+    with pytest.raises(eq.EqError):
+        eq.encode_host(eq.build_tables(sym), 1, 9, 1000, sym, np.ones(9, np.float32), codec=5)
