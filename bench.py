@@ -109,12 +109,13 @@ def counter_record(name: str, key: str, kernel_src: str):
 
 
 def build_block(cfg: int, layer: int = 0, lane_run: int = 8, use_cache: bool = True,
-                tensors=None, whole_rows: bool = False):
+                tensors=None, whole_rows: bool = False, codec: int = 0):
     """Encode one block with the library's host encoder and place its
     containers in device memory (all tensors, or the listed indices). Chunks
     are 64 Ki symbols, or with whole_rows the nearest multiple of the row
-    length (what the fused decode + GEMV needs). With EQ_BENCH_CACHE=<dir> the
-    encoded containers are kept there as .npy files and reused."""
+    length (what the fused decode + GEMV needs). codec 0 = rANS, 1 = Huffman.
+    With EQ_BENCH_CACHE=<dir> the encoded containers are kept there as .npy
+    files and reused."""
     import numpy as np
     import synth
     from rans_decode_amd import eq
@@ -125,7 +126,8 @@ def build_block(cfg: int, layer: int = 0, lane_run: int = 8, use_cache: bool = T
         if tensors is not None and i not in tensors:
             continue
         Z = whole_row_chunk(sp.cols, lane_run) if whole_rows else synth.CHUNK_SYMBOLS
-        path = os.path.join(cache, f"cfg{cfg}_layer{layer}_t{i}_k{lane_run}_z{Z}.npy") if cache else None
+        path = (os.path.join(cache, f"cfg{cfg}_layer{layer}_t{i}_k{lane_run}_z{Z}_c{codec}.npy")
+                if cache else None)
         if path and os.path.exists(path):
             blob = np.load(path)
         else:
@@ -135,7 +137,7 @@ def build_block(cfg: int, layer: int = 0, lane_run: int = 8, use_cache: bool = T
             blob = eq.encode_host(tab, sp.dtype, sp.rows, sp.cols, t.symbols, t.scales,
                                   t.esc_idx if esc else None, t.esc_val if esc else None,
                                   esc_code=t.esc_code if esc else 0,
-                                  chunk_symbols=Z, lane_run=lane_run)
+                                  chunk_symbols=Z, lane_run=lane_run, codec=codec)
             del t
             if path:
                 os.makedirs(cache, exist_ok=True)
@@ -237,6 +239,8 @@ def copy_ceiling(nbytes: int) -> float:
     return 2.0 * nbytes / (ms * 1e-3) / 1e9
 
 
+CODECS = {"rans": 0, "huffman": 1}
+
 WORKLOADS = {
     "block70b": (4, "70B-shaped block decode+dequant: q,o 8192x8192; k,v 1024x8192; gate,up 28672x8192; "
                     "down 8192x28672; int8 2.1-bit Laplace codes, 4 super-weight escapes"),
@@ -254,8 +258,9 @@ def bench_block(args):
     from rans_decode_amd import eq
 
     cfg, what = WORKLOADS[args.workload]
+    codec = CODECS[args.codec]
     t0 = time.perf_counter()
-    specs, conts = build_block(cfg, 0, args.lane_run)
+    specs, conts = build_block(cfg, 0, args.lane_run, codec=codec)
     offs = synth.block_offsets(specs)
     n = offs[-1]
     log(f"block built in {time.perf_counter() - t0:.1f} s: {n} weights, "
@@ -292,7 +297,8 @@ def bench_block(args):
     comp, outb = algorithmic_bytes(conts)
     algo = comp + outb
     achieved = algo / (avg_ms * 1e-3) / 1e9
-    traffic = traffic_record(os.path.join(ROOT, "rans_decode_amd", "csrc", "decode.hip"))
+    traffic = (traffic_record(os.path.join(ROOT, "rans_decode_amd", "csrc", "decode.hip"))
+               if cfg == 4 and codec == 0 else None)
     total_container = sum(c.nbytes for c in conts)
     rec = {
         "metric": "decoded weight GB/s (bf16 out) and % HBM roofline, 70B-shaped block decode"
@@ -309,7 +315,8 @@ def bench_block(args):
         "dtype": "u32/f32",
         "data": "synthetic",
         "config": {
-            "workload": f"{what}; 64Ki-symbol chunks, 64 lanes, K={args.lane_run}, bf16 out",
+            "workload": f"{what}; {args.codec} codec, 64Ki-symbol chunks, 64 lanes, K={args.lane_run}, bf16 out",
+            "codec": args.codec,
             "weights": n,
             "container_bytes": total_container,
             "effective_bits_per_weight": round(8.0 * total_container / n, 4),
@@ -614,6 +621,9 @@ def main():
     ap.add_argument("--no-copy-ceiling", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--layers", type=int, default=80, help="blocks in the model80 workload")
+    ap.add_argument("--codec", choices=sorted(CODECS), default="rans",
+                    help="entropy coder of the block workloads' containers (rANS: EntQuant's ANS; "
+                         "huffman: EntroLLM's coder, for comparison)")
     ap.add_argument("--lane-run", type=int, default=8, choices=[1, 2, 4, 8, 16],
                     help="container lane run K of the encoded block (workload parameter)")
     args = ap.parse_args()

@@ -75,6 +75,7 @@ struct TArgs {
     uint64_t off_scales, off_dir, off_states, off_words, off_esc_idx, off_esc_val, off_freq;
     uint32_t Z, dtype, mode, const_sym;
     uint32_t is_const, wg_begin;
+    uint32_t codec, pad;  // entropy coder: eqfmt::kCodecRans or kCodecHuffman
     const uint16_t *x;  // fused GEMV: the tensor's bf16 input vector [cols]
     float *y;           // fused GEMV: its fp32 output [rows]
 };
@@ -189,7 +190,7 @@ __device__ __forceinline__ void raise_flag(uint32_t *status, uint32_t bits, uint
 // Slot table of the tensor: for every slot in [0, 4096) the byte s with
 // cum[s] <= slot < cum[s] + f[s], packed as s | f << 8 | (slot - cum[s]) << 20
 // (f <= 4095 here; a one-symbol tensor never builds a table).
-__device__ void build_lut(const TArgs &T, LutEnt *lut, uint32_t *cum) {
+__device__ __forceinline__ void build_lut(const TArgs &T, LutEnt *lut, uint32_t *cum) {
     const uint16_t *freq = reinterpret_cast<const uint16_t *>(T.base + T.off_freq);
     const uint32_t tid = threadIdx.x;
     if (tid < 64) {
@@ -228,6 +229,78 @@ __device__ void build_lut(const TArgs &T, LutEnt *lut, uint32_t *cum) {
     __syncthreads();
 }
 
+// Huffman decoding table of the tensor (codec 1), 4096 four-byte entries in
+// the slot-table memory: entry[v] = length | symbol << 24 of the codeword
+// whose bits, first bit in bit 0, are the low `length` bits of v (the
+// canonical code of the length table, codewords of at most 12 bits).
+// Wave 0 ranks the symbols of each length with ballots (bytes ascending) and
+// lays out the canonical tables in `scr`; then every thread resolves its
+// slots by trying the lengths in order (the code is prefix-free, so the
+// first match is the codeword). Slots no codeword covers (impossible for a
+// complete code, which the host checks) take 12 bits and symbol 0.
+__device__ __forceinline__ void build_lut_huff(const uint16_t *tab, uint32_t *lut, uint32_t *scr) {
+    const uint32_t tid = threadIdx.x;
+    constexpr uint32_t L = eqfmt::kHuffMaxLen;
+    uint32_t *sorted = scr;            // [256] symbols in (length, byte) order
+    uint32_t *first = scr + 256;       // [L + 1] first code value of each length
+    uint32_t *cnt = scr + 256 + 16;    // [L + 1] codewords of each length
+    uint32_t *off = scr + 256 + 32;    // [L + 1] index in sorted[] of each length's first
+    if (tid < 64) {
+        uint32_t len[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) len[r] = tab[64 * r + tid];
+        uint32_t c[L + 1] = {}, o[L + 1] = {}, f[L + 1] = {}, run[L + 1] = {};
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (uint32_t l = 1; l <= L; ++l)
+                c[l] += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(len[r] == l));
+        uint32_t code = 0, at = 0;
+#pragma unroll
+        for (uint32_t l = 1; l <= L; ++l) {
+            f[l] = code;
+            o[l] = at;
+            code = (code + c[l]) << 1;
+            at += c[l];
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+#pragma unroll
+            for (uint32_t l = 1; l <= L; ++l) {
+                const uint64_t m = __builtin_amdgcn_ballot_w64(len[r] == l);
+                const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                if (len[r] == l) sorted[o[l] + run[l] + below] = 64u * r + tid;
+                run[l] += (uint32_t)__builtin_popcountll(m);
+            }
+        }
+        if (tid <= L) {
+            uint32_t fv = 0, cv = 0, ov = 0;
+#pragma unroll
+            for (uint32_t l = 0; l <= L; ++l)
+                if (tid == l) { fv = f[l]; cv = c[l]; ov = o[l]; }
+            first[tid] = fv;
+            cnt[tid] = cv;
+            off[tid] = ov;
+        }
+    }
+    __syncthreads();
+    for (uint32_t v = tid; v < 4096u; v += kThreads) {
+        uint32_t e = L;  // fallback: 12 bits, symbol 0
+        const uint32_t rv = __builtin_bitreverse32(v);
+        for (uint32_t l = 1; l <= L; ++l) {
+            const uint32_t code = rv >> (32u - l);  // the low l bits of v, first bit highest
+            const uint32_t i = code - first[l];
+            if (i < cnt[l]) {
+                e = l | (sorted[off[l] + i] << 24);
+                break;
+            }
+        }
+        lut[v] = e;
+    }
+    __syncthreads();
+}
+
 template <uint32_t LW> struct LaneBlock;
 struct uint8x { uint4 a, b; };
 template <> struct LaneBlock<16> { using type = uint8x; };
@@ -256,7 +329,7 @@ __device__ __forceinline__ void put_block(uint16_t *ring, uint32_t b, Blk v, uin
 
 // Per-chunk decoder state of one wave. Positions inside the chunk are u32
 // (a chunk holds at most 2^24 symbols); wave-uniform values stay in SGPRs.
-template <int K, bool BF16, uint32_t DT, int MODE, bool GEMV = false>
+template <int K, bool BF16, uint32_t DT, int MODE, bool GEMV = false, uint32_t CODEC = 0>
 struct Chunk {
     const TArgs &T;
     const LutEnt *lut;
@@ -267,7 +340,8 @@ struct Chunk {
     uint32_t wc, wpad, nblocks, nb;
     const uint16_t *words;
     Blk pend;
-    uint32_t x;    // this lane's rANS state
+    uint32_t x;    // this lane's rANS state, or its Huffman bit buffer (next bit in bit 0)
+    uint32_t nbits;  // Huffman: valid bits in x
     uint32_t ptr;  // words consumed (wave-uniform)
     uint64_t row;  // row of the current group's first symbol (modes 1, 2)
     uint32_t col;  // its column
@@ -312,8 +386,39 @@ struct Chunk {
 
     // One decode step of this lane (inactive lanes keep their state, which is
     // >= 2^16, so they never ask for a word).
+    // Huffman step: a lane holding fewer than 12 bits first takes one word
+    // (ballot + rank as for rANS), then decodes one codeword with one table
+    // read: the entry's low 5 bits are the length, its top byte the symbol.
+    template <bool MASKED>
+    __device__ __forceinline__ uint32_t step_huff(bool active) {
+        const uint32_t *tab = reinterpret_cast<const uint32_t *>(lut);
+        const bool need = (MASKED ? active : true) && nbits < 12u;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(need);
+        const uint32_t rank = __builtin_amdgcn_mbcnt_hi(
+            (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        const uint32_t w = ring[(ptr & (kRing - 1u)) + rank];
+        const uint32_t merged = (w << nbits) | x;
+        uint32_t b, nb;
+        asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(b) : "v"(x), "v"(merged), "s"(m));
+        asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(nb) : "v"(nbits), "v"(nbits + 16u), "s"(m));
+        ptr += (uint32_t)__builtin_popcountll(m);
+        const uint32_t e = tab[b & 4095u];
+        const uint32_t bn = b >> (e & 31u);
+        const uint32_t nn = nb - (e & 0xFFu);
+        if (MASKED) {
+            // a lane past the chunk keeps its final bits for the end check
+            x = active ? bn : b;
+            nbits = active ? nn : nb;
+        } else {
+            x = bn;
+            nbits = nn;
+        }
+        return e;
+    }
+
     template <bool MASKED>
     __device__ __forceinline__ uint32_t step(bool active) {
+        if constexpr (CODEC == eqfmt::kCodecHuffman) return step_huff<MASKED>(active);
         const LutEnt ent = lut[x & 4095u];
         uint32_t xn = ent_next(ent, x);
         if (MASKED) xn = active ? xn : x;
@@ -558,7 +663,10 @@ struct Chunk {
         }
     }
 
-    __device__ void run(uint64_t chunk, void *out, uint32_t *status) {
+    // (always inlined: an outlined copy would take the kernel argument's
+    // address, which makes the compiler copy the whole argument block into
+    // scratch memory)
+    __device__ __forceinline__ void run(uint64_t chunk, void *out, uint32_t *status) {
         const uint8_t *dir = T.base + T.off_dir + chunk * 16u;
         const uint64_t ws = *reinterpret_cast<const uint64_t *>(dir);
         wc = *reinterpret_cast<const uint32_t *>(dir + 8);
@@ -568,7 +676,12 @@ struct Chunk {
             return;
         }
         words = reinterpret_cast<const uint16_t *>(T.base + T.off_words) + ws;
-        x = reinterpret_cast<const uint32_t *>(T.base + T.off_states)[chunk * 64u + lane];
+        if constexpr (CODEC == eqfmt::kCodecHuffman) {
+            x = 0;
+            nbits = 0;
+        } else {
+            x = reinterpret_cast<const uint32_t *>(T.base + T.off_states)[chunk * 64u + lane];
+        }
         nblocks = (wpad + kBlk - 1u) / kBlk;
         nb = 0;
         ptr = 0;
@@ -621,7 +734,8 @@ struct Chunk {
         if (nfull * G < nk) group<true>(nfull, out);
 
         // integrity: every lane back at 2^16 and every word consumed
-        const uint64_t bad = __builtin_amdgcn_ballot_w64(x != 65536u);
+        // (Huffman: every lane's leftover bits must be the zero padding)
+        const uint64_t bad = __builtin_amdgcn_ballot_w64(CODEC == eqfmt::kCodecHuffman ? x != 0u : x != 65536u);
         uint32_t bits = 0;
         if (ptr > wc) bits |= EQ_DEV_WORD_OVERRUN;
         else if (ptr != wc || bad) bits |= EQ_DEV_BAD_END_STATE;
@@ -632,13 +746,16 @@ struct Chunk {
 // One-symbol tensor: every state must be 2^16 and no word stored; the output
 // is the symbol's dequantised value everywhere (escapes patched).
 template <bool BF16>
-__device__ void const_chunk(const TArgs &T, uint64_t chunk, uint32_t lane, void *out,
+__device__ __forceinline__ void const_chunk(const TArgs &T, uint64_t chunk, uint32_t lane, void *out,
                             uint32_t *status) {
     const uint64_t p0 = chunk * T.Z;
     const uint32_t nk = (uint32_t)umin64(T.Z, T.n - p0);
     const uint8_t *dir = T.base + T.off_dir + chunk * 16u;
     const uint32_t wc = *reinterpret_cast<const uint32_t *>(dir + 8);
-    const uint32_t xs = reinterpret_cast<const uint32_t *>(T.base + T.off_states)[chunk * 64u + lane];
+    // (the Huffman codec stores no lane states)
+    const uint32_t xs = T.codec == eqfmt::kCodecRans
+                            ? reinterpret_cast<const uint32_t *>(T.base + T.off_states)[chunk * 64u + lane]
+                            : 65536u;
     const uint64_t bad = __builtin_amdgcn_ballot_w64(xs != 65536u);
     raise_flag(status, (bad || wc) ? EQ_DEV_BAD_END_STATE : 0u, lane);
     const float *sc = reinterpret_cast<const float *>(T.base + T.off_scales);
@@ -670,12 +787,16 @@ __device__ void const_chunk(const TArgs &T, uint64_t chunk, uint32_t lane, void 
 
 // One-symbol tensor, fused GEMV: per row, lanes stride over the columns with
 // the row's weight (super weights substituted where listed), then reduce.
-__device__ void const_chunk_gemv(const TArgs &T, uint64_t chunk, uint32_t lane, uint32_t *status) {
+__device__ __forceinline__ void const_chunk_gemv(const TArgs &T, uint64_t chunk, uint32_t lane,
+                                                 uint32_t *status) {
     const uint64_t p0 = chunk * T.Z;
     const uint32_t nk = (uint32_t)umin64(T.Z, T.n - p0);
     const uint8_t *dir = T.base + T.off_dir + chunk * 16u;
     const uint32_t wc = *reinterpret_cast<const uint32_t *>(dir + 8);
-    const uint32_t xs = reinterpret_cast<const uint32_t *>(T.base + T.off_states)[chunk * 64u + lane];
+    // (the Huffman codec stores no lane states)
+    const uint32_t xs = T.codec == eqfmt::kCodecRans
+                            ? reinterpret_cast<const uint32_t *>(T.base + T.off_states)[chunk * 64u + lane]
+                            : 65536u;
     const uint64_t bad = __builtin_amdgcn_ballot_w64(xs != 65536u);
     raise_flag(status, (bad || wc) ? EQ_DEV_BAD_END_STATE : 0u, lane);
     const float *sc = reinterpret_cast<const float *>(T.base + T.off_scales);
@@ -724,7 +845,13 @@ __global__ void __launch_bounds__(kThreads) k_decode(LArgs a) {
     const bool is_const = T.is_const != 0;
     // the LUT build's cumulative-frequency scratch reuses the (not yet
     // filled) rings
-    if (!is_const) build_lut(T, lut, reinterpret_cast<uint32_t *>(&rings[0][0]));
+    if (!is_const) {
+        if (T.codec == eqfmt::kCodecHuffman)
+            build_lut_huff(reinterpret_cast<const uint16_t *>(T.base + T.off_freq),
+                           reinterpret_cast<uint32_t *>(lut), reinterpret_cast<uint32_t *>(&rings[0][0]));
+        else
+            build_lut(T, lut, reinterpret_cast<uint32_t *>(&rings[0][0]));
+    }
     if (chunk >= T.n_chunks) return;
     if (is_const) {
         if constexpr (GEMV) const_chunk_gemv(T, chunk, lane, a.status);
@@ -733,10 +860,15 @@ __global__ void __launch_bounds__(kThreads) k_decode(LArgs a) {
     }
     const uint64_t p0 = chunk * T.Z;
     const uint32_t nk = (uint32_t)umin64(T.Z, T.n - p0);
+#define EQ_RUN_C(BF, DT, MO, CO)                                                       \
+    do {                                                                               \
+        Chunk<K, BF, DT, MO, GEMV, CO> c{T, lut, rings[wave], lane, p0, nk};           \
+        c.run(chunk, a.out, a.status);                                                 \
+    } while (0)
 #define EQ_RUN(BF, DT, MO)                                                             \
     do {                                                                               \
-        Chunk<K, BF, DT, MO, GEMV> c{T, lut, rings[wave], lane, p0, nk};               \
-        c.run(chunk, a.out, a.status);                                                 \
+        if (T.codec == eqfmt::kCodecHuffman) EQ_RUN_C(BF, DT, MO, eqfmt::kCodecHuffman); \
+        else EQ_RUN_C(BF, DT, MO, eqfmt::kCodecRans);                                  \
     } while (0)
     if constexpr (GEMV) {
         if (T.dtype == EQ_DTYPE_INT8) {
@@ -760,6 +892,7 @@ __global__ void __launch_bounds__(kThreads) k_decode(LArgs a) {
         if (T.mode == M_ROW1) EQ_RUN(false, 0u, M_ROW1); else EQ_RUN(false, 0u, M_GENERAL);
     }
 #undef EQ_RUN
+#undef EQ_RUN_C
 }
 
 // ---------------------------------------------------------------------------
@@ -848,7 +981,8 @@ bool header_ok(const eq_header &h) {
         return false;
     if (h.rows == 0 || h.cols == 0 || h.rows * h.cols != h.n) return false;
     if (h.n_chunks != (h.n + h.chunk_symbols - 1) / h.chunk_symbols) return false;
-    const eqfmt::Sections s = eqfmt::layout(h.rows, h.n_chunks, h.n_words, h.n_esc);
+    if (h.codec != eqfmt::kCodecRans && h.codec != eqfmt::kCodecHuffman) return false;
+    const eqfmt::Sections s = eqfmt::layout(h.rows, h.n_chunks, h.n_words, h.n_esc, h.codec);
     return s.freq == h.off_freq && s.scales == h.off_scales && s.dir == h.off_dir &&
            s.states == h.off_states && s.words == h.off_words && s.esc_idx == h.off_esc_idx &&
            s.esc_val == h.off_esc_val && s.total == h.total_bytes;
@@ -897,6 +1031,8 @@ eq_status launch_block(const eq_block *b, void *out, const uint16_t *const *x, f
             t.off_esc_val = h.off_esc_val;
             t.Z = h.chunk_symbols;
             t.dtype = h.dtype;
+            t.codec = h.codec;
+            t.pad = 0;
             t.is_const = 0;
             t.const_sym = 0;
             if (h.single_symbol >= 0) {

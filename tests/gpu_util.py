@@ -13,14 +13,14 @@ def log(msg):
     print(msg, flush=True)
 
 
-def encode(t: synth.Tensor, chunk_symbols=65536, lane_run=8, tables=None):
+def encode(t: synth.Tensor, chunk_symbols=65536, lane_run=8, tables=None, codec=0):
     sp = t.spec
     tab = tables if tables is not None else eq.build_tables(t.symbols)
     esc = t.esc_idx.size > 0
     return eq.encode_host(tab, sp.dtype, sp.rows, sp.cols, t.symbols, t.scales,
                           t.esc_idx if esc else None, t.esc_val if esc else None,
                           esc_code=t.esc_code if esc else 0, chunk_symbols=chunk_symbols,
-                          lane_run=lane_run)
+                          lane_run=lane_run, codec=codec)
 
 
 class Packed:
