@@ -455,6 +455,99 @@ def bench_gemv(args):
     print(json.dumps(rec), flush=True)
 
 
+def bench_encode(args):
+    """Device-side encode (eq_encode_device) of the 70B-shaped block's seven
+    tensors, symbols and scales already in HBM; each container is checked
+    byte-for-byte against the host encoder's. Next to it: the host encoder
+    (eq_encode_host, all host cores) on the same tensors."""
+    import numpy as np
+    import torch
+    import synth
+    from rans_decode_amd import eq
+
+    specs = synth.config_specs(4)
+    tensors = []
+    t0 = time.perf_counter()
+    for i, sp in enumerate(specs):
+        t = synth.make_tensor(4, 0, i)
+        esc = t.esc_idx.size > 0
+        tensors.append(dict(
+            spec=sp, sym=torch.from_numpy(t.symbols).cuda(), sc=torch.from_numpy(t.scales).cuda(),
+            ei=torch.from_numpy(t.esc_idx.astype(np.int64)).cuda() if esc else None,
+            ev=torch.from_numpy(t.esc_val.view(np.int16)).cuda() if esc else None,
+            code=t.esc_code if esc else 0))
+    log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
+    wsb = max(int(eq._lib.eq_encode_device_workspace(sp.rows, sp.cols, synth.CHUNK_SYMBOLS)) for sp in specs)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    outs = [torch.empty(int(eq._lib.eq_encode_device_bound(sp.rows, sp.cols, synth.CHUNK_SYMBOLS, sp.n_esc)),
+                        dtype=torch.uint8, device="cuda") for sp in specs]
+    stream = torch.cuda.current_stream()
+    lens, stats = [], []
+
+    def block():
+        lens.clear()
+        stats.clear()
+        for d, o in zip(tensors, outs):
+            sp = d["spec"]
+            _, ln, st = eq.eq_encode_device(sp.dtype, sp.rows, sp.cols, d["sym"], d["sc"], d["ei"], d["ev"],
+                                            d["code"], synth.CHUNK_SYMBOLS, args.lane_run, workspace=ws,
+                                            out=o, stream=stream)
+            lens.append(ln)
+            stats.append(st)
+
+    for _ in range(args.warmup):
+        block()
+    torch.cuda.synchronize()
+    if any(int(st.item()) for st in stats):
+        raise RuntimeError("device encode flagged its input")
+    # byte-for-byte against the host encoder (its containers, built or cached)
+    _, host = build_block(4, 0, args.lane_run)
+    for i, (c, o, ln) in enumerate(zip(host, outs, lens)):
+        got = o[:int(ln.item())].cpu().numpy()
+        if got.size != c.host.size or not np.array_equal(got, c.host):
+            raise RuntimeError(f"tensor {i}: device container differs from the host encoder's")
+    log("device containers byte-identical to the host encoder's")
+    ms = []
+    for _ in range(args.steps):
+        s0, e0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        block()
+        e0.record(stream)
+        torch.cuda.synchronize()
+        ms.append(s0.elapsed_time(e0))
+    # the host encoder (eq_build_tables + eq_encode_host, all host cores) on
+    # the same tensors, one pass
+    host_enc_s = 0.0
+    for i, sp in enumerate(specs):
+        t = synth.make_tensor(4, 0, i)
+        esc = t.esc_idx.size > 0
+        t_enc0 = time.perf_counter()
+        tab = eq.build_tables(t.symbols)
+        eq.encode_host(tab, sp.dtype, sp.rows, sp.cols, t.symbols, t.scales, t.esc_idx if esc else None,
+                       t.esc_val if esc else None, esc_code=t.esc_code if esc else 0,
+                       chunk_symbols=synth.CHUNK_SYMBOLS, lane_run=args.lane_run)
+        host_enc_s += time.perf_counter() - t_enc0
+        del t
+    n = sum(sp.n for sp in specs)
+    f = float(np.mean(ms))
+    rec = {
+        "metric": "device-side encode of the 70B-shaped block (histogram, quantiser, rANS encode, container)",
+        "value": round(n / (f * 1e-3) / 1e9, 2), "unit": "G symbols/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(f, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "u32", "data": "synthetic",
+        "config": {"workload": "70B-shaped block, 855,638,016 int8 codes (2.1-bit Laplace), 4 super weights, "
+                               f"64 Ki chunks, K={args.lane_run}; one eq_encode_device call per tensor",
+                   "weights": n},
+        "kernel_ms": {"mean": round(f, 4), "median": round(float(np.median(ms)), 4),
+                      "min": round(float(np.min(ms)), 4)},
+        "host_encoder_s": round(host_enc_s, 3),
+        "host_encoder_G_symbols_per_s": round(n / host_enc_s / 1e9, 3),
+        "host_cores": host_cores(),
+        "speedup_vs_host_encoder": round(host_enc_s * 1e3 / f, 1),
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def bench_model(args):
     """80 blocks of the 70B-shaped layer, resident as containers (about 18 GB);
     each token pass decodes block b into bf16 buffer b % 2 on one stream
@@ -615,7 +708,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", choices=["block70b", "model80", "gemv70b", "cfg1", "cfg2", "cfg3"],
+    ap.add_argument("--workload", choices=["block70b", "model80", "gemv70b", "encode70b", "cfg1", "cfg2",
+                                           "cfg3"],
                     default="block70b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-ceiling", action="store_true")
@@ -640,6 +734,8 @@ def main():
         bench_model(args)
     elif args.workload == "gemv70b":
         bench_gemv(args)
+    elif args.workload == "encode70b":
+        bench_encode(args)
     else:
         bench_block(args)
 

@@ -105,6 +105,7 @@ typedef int32_t eq_status;
 /* Device status bits (ORed into eq_block.d_status). */
 #define EQ_DEV_BAD_END_STATE 1u /* a lane did not end at 2^16, or words left over */
 #define EQ_DEV_WORD_OVERRUN 2u  /* a chunk read past its word count / bad dir entry */
+#define EQ_DEV_BAD_INPUT 4u     /* eq_encode_device: invalid symbols, escapes or scales */
 
 #define EQ_DTYPE_INT8 1u /* two's-complement int8 codes */
 #define EQ_DTYPE_E4M3 2u /* OCP FP8 E4M3FN codes */
@@ -248,6 +249,34 @@ eq_status eq_decode_dequant_bf16(const eq_block *b, uint16_t *d_bf16, void *stre
  */
 eq_status eq_decode_gemv_bf16(const eq_block *b, const uint16_t *const *d_x, float *const *d_y,
                               void *stream);
+
+/*
+ * eq_encode_device -- the encoder of eq_encode_host (rANS codec) on the GPU:
+ * histogram, the same 12-bit quantiser (as eq_build_tables), chunk-parallel
+ * interleaved encoding, container assembly; the container is byte-for-byte
+ * what eq_encode_host(eq_build_tables(symbols), d, ...) writes. This is the
+ * offline ANS compression of technical component 2 of the EntQuant summary
+ * (flatten, ANS-compress, store bitstream + scales + metadata), done where
+ * the weights already are.
+ * d: as for eq_encode_host (codec must be EQ_CODEC_RANS, else
+ *    EQ_EUNSUPPORTED). Device pointers: d_symbols (rows*cols bytes, 16-byte
+ *    aligned), d_scales (rows fp32), d_esc_idx / d_esc_bf16 (n_esc entries,
+ *    may be NULL when n_esc == 0), d_workspace (workspace_bytes >=
+ *    eq_encode_device_workspace(), 16-byte aligned, contents ignored), d_out
+ *    (cap >= eq_encode_device_bound(), 16-byte aligned), d_out_len (device u64
+ *    receiving the container size; may be NULL), d_status (device u32, caller
+ *    zeroed, may be NULL: EQ_DEV_BAD_INPUT when a symbol, escape list or
+ *    scale is invalid; the container is then unspecified).
+ * Enqueues seven kernels on stream; never allocates or synchronises.
+ * Errors: EQ_EINVAL (arguments), EQ_ERANGE (workspace or cap too small),
+ * EQ_EUNSUPPORTED (codec), EQ_EHIP (launch).
+ */
+uint64_t eq_encode_device_bound(uint64_t rows, uint64_t cols, uint32_t chunk_symbols, uint64_t n_esc);
+uint64_t eq_encode_device_workspace(uint64_t rows, uint64_t cols, uint32_t chunk_symbols);
+eq_status eq_encode_device(const eq_tensor_desc *d, const uint8_t *d_symbols, const float *d_scales,
+                           const uint64_t *d_esc_idx, const uint16_t *d_esc_bf16, uint64_t n_esc,
+                           void *d_workspace, uint64_t workspace_bytes, void *d_out, uint64_t cap,
+                           uint64_t *d_out_len, uint32_t *d_status, void *stream);
 
 /*
  * eq_gemv_bf16 -- y[r] = sum_c W[r, c] * x[c] for a row-major bf16 [rows,

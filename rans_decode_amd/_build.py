@@ -33,9 +33,11 @@ def build_library(verbose: bool = False, out: str = LIB, defines: dict | None = 
     dflags = [f"-D{k}={v}" for k, v in (defines or {}).items()]
     _run(["g++", "-O2", "-std=c++17", "-fPIC", "-pthread", "-Wall", "-Wextra",
           "-c", os.path.join(CSRC, "host_codec.cpp"), "-o", host_o], verbose)
+    enc_o = os.path.join(build_dir, "encode.o")
     _run(["hipcc", *HIPCC_FLAGS, *dflags, "-c", os.path.join(CSRC, "decode.hip"), "-o", dev_o], verbose)
+    _run(["hipcc", *HIPCC_FLAGS, *dflags, "-c", os.path.join(CSRC, "encode.hip"), "-o", enc_o], verbose)
     tmp = out + ".tmp"
-    _run(["hipcc", "-shared", f"--offload-arch={ARCH}", host_o, dev_o, "-o", tmp, "-pthread"], verbose)
+    _run(["hipcc", "-shared", f"--offload-arch={ARCH}", host_o, dev_o, enc_o, "-o", tmp, "-pthread"], verbose)
     os.replace(tmp, out)
     return out
 

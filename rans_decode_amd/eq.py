@@ -80,11 +80,17 @@ def _load():
         "eq_pipeline_run": [_vp, P(eq_block), _u32, _vp, _vp, _vp, _vp, _vp, _vp],
         "eq_pipeline_destroy": [_vp],
         "eq_bf16_from_f32": [_vp, _u64, _vp, _vp],
+        "eq_encode_device": [P(eq_tensor_desc), _vp, _vp, _vp, _vp, _u64, _vp, _u64, _vp, _u64, _vp, _vp, _vp],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
         fn.restype = ctypes.c_int32
         fn.argtypes = args
+    for name in ("eq_encode_device_bound", "eq_encode_device_workspace"):
+        fn = getattr(L, name)
+        fn.restype = _u64
+    L.eq_encode_device_bound.argtypes = [_u64, _u64, _u32, _u64]
+    L.eq_encode_device_workspace.argtypes = [_u64, _u64, _u32]
     L.eq_status_string.restype = ctypes.c_char_p
     L.eq_status_string.argtypes = [ctypes.c_int32]
     return L
@@ -330,3 +336,34 @@ class Pipeline:
             self.close()
         except Exception:
             pass
+
+
+EQ_DEV_BAD_INPUT = 4
+
+
+def eq_encode_device(dtype: int, rows: int, cols: int, d_symbols, d_scales, d_esc_idx=None,
+                     d_esc_val=None, esc_code: int = 0, chunk_symbols: int = 65536, lane_run: int = 8,
+                     workspace=None, out=None, stream=None):
+    """Device-side encode (torch tensors on the GPU). Returns (out, d_len,
+    d_status) without synchronising: out[:int(d_len)] is the container once
+    the stream has run."""
+    torch = _torch()
+    n_esc = 0 if d_esc_idx is None else int(d_esc_idx.numel())
+    d = eq_tensor_desc(dtype=dtype, lane_run=lane_run, rows=rows, cols=cols,
+                       chunk_symbols=chunk_symbols, esc_enabled=1 if n_esc or esc_code else 0,
+                       esc_code=esc_code, codec=EQ_CODEC_RANS)
+    dev = d_symbols.device
+    wsb = int(_lib.eq_encode_device_workspace(rows, cols, chunk_symbols))
+    cap = int(_lib.eq_encode_device_bound(rows, cols, chunk_symbols, n_esc))
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty(max(cap, 16), dtype=torch.uint8, device=dev)
+    d_len = torch.zeros(1, dtype=torch.int64, device=dev)
+    d_status = torch.zeros(1, dtype=torch.int32, device=dev)
+    _check("eq_encode_device", _lib.eq_encode_device(
+        ctypes.byref(d), d_symbols.data_ptr(), d_scales.data_ptr(),
+        d_esc_idx.data_ptr() if n_esc else None, d_esc_val.data_ptr() if n_esc else None, n_esc,
+        workspace.data_ptr(), workspace.numel(), out.data_ptr(), out.numel(), d_len.data_ptr(),
+        d_status.data_ptr(), _stream_handle(stream)))
+    return out, d_len, d_status

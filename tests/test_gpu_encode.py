@@ -1,0 +1,122 @@
+"""GPU device-side encoder (`eq_encode_device`) against the host encoder:
+the containers must be byte-identical to eq_encode_host(eq_build_tables(s))
+(which the CPU tests pin byte-for-byte to the oracle's encoder), and a
+GPU decode of them must reproduce the original symbols."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from conftest import gpu_available
+from gpu_util import assert_same, log, run_u8
+from rans_decode_amd import eq
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")]
+
+
+def _dev(a, dtype):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda") if a is not None else None
+
+
+def device_container(sym, scales, dtype, rows, cols, Z, K, esc_idx=None, esc_val=None, esc_code=0):
+    ds = _dev(sym, None)
+    dsc = _dev(scales.astype(np.float32), None)
+    di = _dev(esc_idx.astype(np.int64), None) if esc_idx is not None and len(esc_idx) else None
+    dv = _dev(esc_val.view(np.int16), None) if esc_val is not None and len(esc_val) else None
+    out, d_len, st = eq.eq_encode_device(dtype, rows, cols, ds, dsc, di, dv, esc_code, Z, K)
+    torch.cuda.synchronize()
+    n = int(d_len.item())
+    return out[:n].cpu().numpy(), int(st.item())
+
+
+def host_container(sym, scales, dtype, rows, cols, Z, K, esc_idx=None, esc_val=None, esc_code=0):
+    return eq.encode_host(eq.build_tables(sym), dtype, rows, cols, sym, scales,
+                          esc_idx if esc_idx is not None and len(esc_idx) else None,
+                          esc_val if esc_val is not None and len(esc_val) else None,
+                          esc_code=esc_code, chunk_symbols=Z, lane_run=K)
+
+
+def check_equal(sym, scales, dtype, rows, cols, Z=65536, K=8, esc_idx=None, esc_val=None, esc_code=0,
+                what=""):
+    got, st = device_container(sym, scales, dtype, rows, cols, Z, K, esc_idx, esc_val, esc_code)
+    assert st == 0, f"{what}: device status {st}"
+    exp = host_container(sym, scales, dtype, rows, cols, Z, K, esc_idx, esc_val, esc_code)
+    assert got.size == exp.size, f"{what}: size {got.size} vs {exp.size}"
+    bad = np.flatnonzero(got != exp)
+    assert bad.size == 0, f"{what}: {bad.size} bytes differ, first at {bad[0]}"
+    return got
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_config_matrices(cfg):
+    t = synth.make_tensor(cfg, 0, 0)
+    sp = t.spec
+    log(f"case device encode config {cfg}")
+    c = check_equal(t.symbols, t.scales, sp.dtype, sp.rows, sp.cols, what=f"config {cfg}")
+    sym, st = run_u8([eq.DeviceContainer(c, device="cuda")], sp.n)
+    assert st == 0
+    assert_same(sym, t.symbols, "round trip")
+
+
+def test_block_tensors_with_escapes_and_e4m3():
+    for cfg, i in [(4, 6), (4, 1), (3, 0), (3, 5)]:
+        t = synth.make_tensor(cfg, 0, i)
+        sp = t.spec
+        log(f"case device encode config {cfg} tensor {sp.name}")
+        esc = t.esc_idx.size > 0
+        check_equal(t.symbols, t.scales, sp.dtype, sp.rows, sp.cols,
+                    esc_idx=t.esc_idx if esc else None, esc_val=t.esc_val if esc else None,
+                    esc_code=t.esc_code if esc else 0, what=f"cfg {cfg} {sp.name}")
+        del t
+
+
+def test_random_layouts():
+    rng = np.random.default_rng(31)
+    for it in range(80):
+        K = int(rng.choice([1, 2, 4, 8, 16]))
+        Z = 64 * K * int(rng.integers(1, 9))
+        n = int(rng.integers(1, 5 * Z))
+        n = max(16, n - n % 16) if it % 2 else n
+        k = int(rng.integers(1, 60))
+        present = rng.choice(256, size=k, replace=False)
+        w = rng.exponential(1.0, k) ** 3 + 1e-6
+        sym = present[rng.choice(k, size=n, p=w / w.sum())].astype(np.uint8)
+        divs = [d for d in range(1, min(n, 64) + 1) if n % d == 0]
+        rows = int(rng.choice(divs))
+        scales = rng.uniform(-2, 2, rows).astype(np.float32)
+        check_equal(sym, scales, 1, rows, n // rows, Z, K, what=f"random {it} K={K} Z={Z} n={n}")
+
+
+def test_quantiser_excess_and_ties_and_single_symbol():
+    rng = np.random.default_rng(2)
+    # 200 rare symbols (each rounds up to f = 1) force an excess taken from the largest f
+    sym = np.concatenate([np.zeros(10**6, np.uint8), np.arange(1, 201, dtype=np.uint8),
+                          np.full(3000, 250, np.uint8)])
+    sym = sym[rng.permutation(sym.size)]
+    sym = sym[: sym.size - sym.size % 64]
+    check_equal(sym, np.ones(64, np.float32), 1, 64, sym.size // 64, 16384, 8, what="excess")
+    # equal counts: remainders tie, smaller byte first
+    sym = np.tile(np.arange(7, dtype=np.uint8), 3000)
+    check_equal(sym, np.ones(3, np.float32), 1, 3, 7000, 4096, 4, what="ties")
+    sym = np.full(5000, 0x42, np.uint8)
+    c = check_equal(sym, np.ones(50, np.float32), 1, 50, 100, 512, 8, what="single symbol")
+    assert eq.parse_header(c).single_symbol == 0x42
+
+
+def test_bad_inputs_raise_the_device_flag():
+    sym = np.zeros(4096, np.uint8)
+    sym[10] = 0x80
+    idx = np.array([10], np.uint64)
+    val = np.array([0x4000], np.uint16)
+    _, st = device_container(sym, np.ones(4, np.float32), 1, 4, 1024, 4096, 8, idx, val, 0x80)
+    assert st == 0
+    _, st = device_container(sym, np.ones(4, np.float32), 1, 4, 1024, 4096, 8,
+                             np.array([11], np.uint64), val, 0x80)
+    assert st & eq.EQ_DEV_BAD_INPUT  # listed index does not hold the code
+    _, st = device_container(sym, np.array([1, np.inf, 1, 1], np.float32), 1, 4, 1024, 4096, 8, idx, val, 0x80)
+    assert st & eq.EQ_DEV_BAD_INPUT  # non-finite scale
+    sym2 = np.zeros(4096, np.uint8)
+    sym2[5] = 0x7F
+    _, st = device_container(sym2, np.ones(4, np.float32), 2, 4, 1024, 4096, 8)
+    assert st & eq.EQ_DEV_BAD_INPUT  # E4M3 NaN code, not an escape
