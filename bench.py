@@ -548,6 +548,63 @@ def bench_encode(args):
     print(json.dumps(rec), flush=True)
 
 
+def bench_drift(args):
+    """Adaptive tables: one 28672 x 8192 int8 tensor whose rows come in 16
+    bands of different entropy (0.8 / 2.1 / 3.2 / 1.4 bits, repeating),
+    encoded with one table and with one table per 8 chunks; container size
+    and decode + dequant time of each."""
+    import numpy as np
+    import torch
+    import synth
+    from rans_decode_amd import eq
+
+    t = synth.drift_tensor(28672, 8192, bands=16)
+    n = t.spec.n
+    res = {}
+    for name, seg in (("one_table", 0), ("per_8_chunks", 8)):
+        blob = eq.encode_host(eq.build_tables(t.symbols) if not seg else None, t.spec.dtype, t.spec.rows,
+                              t.spec.cols, t.symbols, t.scales, chunk_symbols=synth.CHUNK_SYMBOLS,
+                              lane_run=args.lane_run, seg_chunks=seg)
+        c = eq.DeviceContainer(blob, device="cuda")
+        out = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        blk = eq.Block([c], None, status)
+        for _ in range(args.warmup):
+            eq.eq_decode_dequant_bf16(blk, out)
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(args.steps):
+            s0, e0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s0.record()
+            eq.eq_decode_dequant_bf16(blk, out)
+            e0.record()
+            torch.cuda.synchronize()
+            ms.append(s0.elapsed_time(e0))
+        if int(status.item()):
+            raise RuntimeError(f"device status {int(status.item())}")
+        sym = torch.empty(n, dtype=torch.uint8, device="cuda")
+        eq.eq_decode_block(blk, sym)
+        torch.cuda.synchronize()
+        if not np.array_equal(sym.cpu().numpy(), t.symbols):
+            raise RuntimeError("decoded symbols differ from the encoded ones")
+        f = float(np.mean(ms))
+        res[name] = {"container_bytes": int(blob.size), "bits_per_weight": round(8.0 * blob.size / n, 4),
+                     "kernel_ms": round(f, 4), "bf16_GBps": round(2 * n / (f * 1e-3) / 1e9, 1)}
+        del c, out, sym
+    rec = {
+        "metric": "adaptive (per-segment) frequency tables vs one table on a tensor with drifting statistics",
+        "value": round(res["one_table"]["container_bytes"] / res["per_8_chunks"]["container_bytes"], 4),
+        "unit": "size ratio (one table / per-segment)", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": res["per_8_chunks"]["kernel_ms"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "u32/f32", "data": "synthetic",
+        "config": {"workload": "28672 x 8192 int8, 16 row bands of 0.8/2.1/3.2/1.4-bit discrete Laplace, "
+                               f"64 Ki chunks, K={args.lane_run}",
+                   "empirical_entropy_bits": round(synth.empirical_entropy(t.symbols), 4)},
+        "one_table": res["one_table"], "per_8_chunks": res["per_8_chunks"],
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def bench_model(args):
     """80 blocks of the 70B-shaped layer, resident as containers (about 18 GB);
     each token pass decodes block b into bf16 buffer b % 2 on one stream
@@ -708,8 +765,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", choices=["block70b", "model80", "gemv70b", "encode70b", "cfg1", "cfg2",
-                                           "cfg3"],
+    ap.add_argument("--workload", choices=["block70b", "model80", "gemv70b", "encode70b", "drift", "cfg1",
+                                           "cfg2", "cfg3"],
                     default="block70b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-ceiling", action="store_true")
@@ -736,6 +793,8 @@ def main():
         bench_gemv(args)
     elif args.workload == "encode70b":
         bench_encode(args)
+    elif args.workload == "drift":
+        bench_drift(args)
     else:
         bench_block(args)
 

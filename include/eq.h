@@ -73,6 +73,11 @@
  *        bitstream has ended), then every active lane decodes one codeword;
  *      - a chunk is valid iff all its words are taken and every lane's
  *        leftover bits are zero.
+ *  - adaptive tables (flags bit 1, rANS only): header offset 148 u32
+ *    seg_chunks (a multiple of 8); chunks are grouped into segments of
+ *    seg_chunks consecutive chunks, each coded with its own 12-bit table
+ *    (the quantiser above on the segment's counts); the freq section holds
+ *    the ceil(n_chunks / seg_chunks) tables in order, 512 bytes each.
  *
  * CONVENTIONS
  *  - Every function returns an eq_status; no exception crosses the ABI.
@@ -134,6 +139,8 @@ typedef struct eq_tensor_desc {
     uint32_t esc_enabled;   /* 1: stream carries super-weight escapes */
     uint32_t esc_code;      /* the escape byte (used when esc_enabled) */
     uint32_t codec;         /* EQ_CODEC_RANS (0) or EQ_CODEC_HUFFMAN */
+    uint32_t seg_chunks;    /* 0: one table per tensor; else chunks per table (a multiple of 8, rANS) */
+    uint32_t reserved;      /* 0 */
 } eq_tensor_desc;
 
 /* Parsed, validated container header (host copy). */
@@ -143,7 +150,7 @@ typedef struct eq_header {
     uint32_t esc_code;
     int32_t single_symbol; /* byte of a one-symbol tensor (f = 4096 / zero-bit code), else -1 */
     uint32_t codec;        /* EQ_CODEC_RANS or EQ_CODEC_HUFFMAN */
-    uint32_t reserved;     /* 0 */
+    uint32_t seg_chunks;   /* chunks per frequency table (adaptive tables), 0 = one table */
     uint64_t off_freq, off_scales, off_dir, off_states, off_words, off_esc_idx, off_esc_val;
     uint64_t total_bytes;
 } eq_header;
@@ -180,7 +187,9 @@ eq_status eq_build_tables(const uint8_t *symbols, uint64_t n, eq_tables *out);
  * t: tables whose freq covers every symbol present (eq_build_tables output or
  *    any valid table); with d->codec = EQ_CODEC_HUFFMAN the code lengths are
  *    derived from t->counts instead (EntroLLM method item 2), so every
- *    present symbol needs a nonzero count; d: shape and layout; symbols: rows*cols bytes; scales:
+ *    present symbol needs a nonzero count; with d->seg_chunks > 0 (adaptive
+ *    tables) each segment's table is quantised from its own counts and t is
+ *    not read (may be NULL); d: shape and layout; symbols: rows*cols bytes; scales:
  *    rows finite fp32; esc_idx / esc_bf16: n_esc strictly ascending flat
  *    indices and their bf16 bits (NULL when n_esc == 0).
  * out / cap: caller's buffer. If out is NULL or cap is too small the call
@@ -258,8 +267,8 @@ eq_status eq_decode_gemv_bf16(const eq_block *b, const uint16_t *const *d_x, flo
  * offline ANS compression of technical component 2 of the EntQuant summary
  * (flatten, ANS-compress, store bitstream + scales + metadata), done where
  * the weights already are.
- * d: as for eq_encode_host (codec must be EQ_CODEC_RANS, else
- *    EQ_EUNSUPPORTED). Device pointers: d_symbols (rows*cols bytes, 16-byte
+ * d: as for eq_encode_host (codec EQ_CODEC_RANS with one table per tensor,
+ *    else EQ_EUNSUPPORTED). Device pointers: d_symbols (rows*cols bytes, 16-byte
  *    aligned), d_scales (rows fp32), d_esc_idx / d_esc_bf16 (n_esc entries,
  *    may be NULL when n_esc == 0), d_workspace (workspace_bytes >=
  *    eq_encode_device_workspace(), 16-byte aligned, contents ignored), d_out

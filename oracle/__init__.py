@@ -51,6 +51,9 @@ def lib():
         "or_encode_codec": (ctypes.c_int, [_U32, _U32, _U64, _U64, _P, _P, _P, _U32, _U32, _U32,
                                            ctypes.c_uint8, _P, _P, _U64,
                                            ctypes.POINTER(_P), ctypes.POINTER(_U64)]),
+        "or_encode_seg": (ctypes.c_int, [_U32, _U32, _U64, _U64, _P, _P, _P, _U32, _U32, _U32, _U32,
+                                         ctypes.c_uint8, _P, _P, _U64,
+                                         ctypes.POINTER(_P), ctypes.POINTER(_U64)]),
         "or_huff_lengths": (ctypes.c_int, [_P, _U32, _P]),
         "or_huff_codes": (ctypes.c_int, [_P, _P]),
         "or_free": (None, [_P]),
@@ -172,21 +175,22 @@ def huff_codes(table) -> np.ndarray:
 def encode(dtype: int, rows: int, cols: int, symbols: np.ndarray, scales: np.ndarray,
            freq: np.ndarray, chunk_symbols: int = 65536, lane_run: int = 8,
            esc_enabled: bool = False, esc_code: int = 0, esc_idx=None, esc_val=None,
-           codec: int = CODEC_RANS) -> np.ndarray:
+           codec: int = CODEC_RANS, seg_chunks: int = 0) -> np.ndarray:
     """Container v1 bytes (np.uint8). freq is the rANS frequency table, or for
-    codec=CODEC_HUFF the code-length table."""
+    codec=CODEC_HUFF the code-length table; with seg_chunks > 0 (adaptive
+    tables) freq is [n_segments, 256], one table per seg_chunks chunks."""
     symbols = np.ascontiguousarray(symbols, dtype=np.uint8)
     scales = np.ascontiguousarray(scales, dtype=np.float32)
-    freq = np.ascontiguousarray(freq, dtype=np.uint16)
+    freq = np.ascontiguousarray(freq, dtype=np.uint16).reshape(-1)
     esc_idx = np.ascontiguousarray(esc_idx if esc_idx is not None else [], dtype=np.uint64)
     esc_val = np.ascontiguousarray(esc_val if esc_val is not None else [], dtype=np.uint16)
     assert symbols.size == rows * cols and scales.size == rows and esc_idx.size == esc_val.size
     out = _P()
     n = _U64()
-    rc = lib().or_encode_codec(codec, dtype, rows, cols, symbols.ctypes.data, scales.ctypes.data,
-                               freq.ctypes.data, chunk_symbols, lane_run, int(esc_enabled), esc_code,
-                               esc_idx.ctypes.data, esc_val.ctypes.data, esc_idx.size,
-                               ctypes.byref(out), ctypes.byref(n))
+    rc = lib().or_encode_seg(codec, dtype, rows, cols, symbols.ctypes.data, scales.ctypes.data,
+                             freq.ctypes.data, seg_chunks, chunk_symbols, lane_run, int(esc_enabled),
+                             esc_code, esc_idx.ctypes.data, esc_val.ctypes.data, esc_idx.size,
+                             ctypes.byref(out), ctypes.byref(n))
     if rc:
         raise OracleError(f"or_encode: {rc}")
     try:
@@ -197,13 +201,13 @@ def encode(dtype: int, rows: int, cols: int, symbols: np.ndarray, scales: np.nda
 
 
 def header(container: np.ndarray) -> dict:
-    v = np.zeros(20, dtype=np.uint64)
+    v = np.zeros(21, dtype=np.uint64)
     rc = lib().or_header_fields(container.ctypes.data, container.size, v.ctypes.data)
     if rc:
         raise OracleError(f"or_header_fields: {rc}")
     keys = ("dtype", "flags", "rows", "cols", "n", "chunk_symbols", "lane_run", "n_chunks",
             "n_esc", "esc_code", "n_words", "off_freq", "off_scales", "off_dir", "off_states",
-            "off_words", "off_esc_idx", "off_esc_val", "total", "codec")
+            "off_words", "off_esc_idx", "off_esc_val", "total", "codec", "seg_chunks")
     return {k: int(x) for k, x in zip(keys, v)}
 
 

@@ -64,6 +64,7 @@
 #define OR_DTYPE_INT8 1u
 #define OR_DTYPE_E4M3 2u
 #define OR_FLAG_ESC 1u
+#define OR_FLAG_SEG 2u        /* one frequency table per segment of chunks */
 #define OR_LANES 64u
 #define OR_PROB_BITS 12u
 #define OR_M 4096u            /* 2^12: sum of the quantised frequencies */
@@ -578,7 +579,13 @@ static uint32_t huff_decode_chunk(const uint8_t *words_le, uint64_t nwords, uint
  *  80 off_freq  88 off_scales  96 off_dir  104 off_states  112 off_words
  * 120 off_esc_idx  128 off_esc_val  136 total_bytes   (all u64 byte offsets)
  * 144 u32 codec: 0 rANS (this section's coder), 1 Huffman (further below)
- * 148..255 zero.
+ * 148 u32 segment size in chunks (flags bit 1; 0 otherwise)
+ * 152..255 zero.
+ * Adaptive tables (flags bit 1, rANS only): the chunks are grouped into
+ * segments of `seg` consecutive chunks (seg a multiple of 8) and each
+ * segment is coded with its own 12-bit table; the freq section then holds
+ * the tables of all segments in order (512 bytes each). Nothing else
+ * changes: the chunk coder is the same, with the segment's table.
  * Sections, each starting on a 256-byte boundary, gaps zero:
  *   freq[256] u16 | scales[rows] f32 | dir[n_chunks] {u64 word_start,
  *   u32 word_count, u32 0} | states[n_chunks][64] u32 | words u16 (each
@@ -588,7 +595,7 @@ static uint32_t huff_decode_chunk(const uint8_t *words_le, uint64_t nwords, uint
  */
 
 typedef struct {
-    uint32_t dtype, flags, Z, K, codec;
+    uint32_t dtype, flags, Z, K, codec, seg;
     uint64_t rows, cols, n, n_chunks, n_esc, n_words;
     uint8_t esc_code;
     uint64_t off_freq, off_scales, off_dir, off_states, off_words, off_esc_idx, off_esc_val,
@@ -633,26 +640,48 @@ void or_free(void *p) { free(p); }
  * esc_*: super-weight side list ([EQ] technical component 4), only with
  * esc_enabled; the stream holds esc_code exactly at the listed indices.
  * On success *out is a malloc'd buffer of *out_len bytes (free with or_free). */
+int or_encode_seg(uint32_t codec, uint32_t dtype, uint64_t rows, uint64_t cols, const uint8_t *sym,
+                  const float *scales, const uint16_t *tables, uint32_t seg, uint32_t Z, uint32_t K,
+                  uint32_t esc_enabled, uint8_t esc_code, const uint64_t *esc_idx,
+                  const uint16_t *esc_val, uint64_t n_esc, uint8_t **out, uint64_t *out_len);
+
 int or_encode_codec(uint32_t codec, uint32_t dtype, uint64_t rows, uint64_t cols, const uint8_t *sym,
                     const float *scales, const uint16_t table[256], uint32_t Z, uint32_t K,
                     uint32_t esc_enabled, uint8_t esc_code, const uint64_t *esc_idx,
                     const uint16_t *esc_val, uint64_t n_esc, uint8_t **out, uint64_t *out_len) {
+    return or_encode_seg(codec, dtype, rows, cols, sym, scales, table, 0, Z, K, esc_enabled, esc_code,
+                         esc_idx, esc_val, n_esc, out, out_len);
+}
+
+/* As or_encode_codec; with seg > 0 (rANS only, a multiple of 8) `tables`
+ * holds one frequency table per segment of seg chunks (ceil(n_chunks / seg)
+ * tables of 256 entries) and chunk k is coded with table k / seg. */
+int or_encode_seg(uint32_t codec, uint32_t dtype, uint64_t rows, uint64_t cols, const uint8_t *sym,
+                  const float *scales, const uint16_t *tables, uint32_t seg, uint32_t Z, uint32_t K,
+                  uint32_t esc_enabled, uint8_t esc_code, const uint64_t *esc_idx,
+                  const uint16_t *esc_val, uint64_t n_esc, uint8_t **out, uint64_t *out_len) {
     *out = NULL;
     *out_len = 0;
     if (codec != OR_CODEC_RANS && codec != OR_CODEC_HUFF) return OR_EINVAL;
+    if (seg && (codec != OR_CODEC_RANS || seg % 8)) return OR_EINVAL;
     if (dtype != OR_DTYPE_INT8 && dtype != OR_DTYPE_E4M3) return OR_EINVAL;
     if (rows == 0 || cols == 0) return OR_EINVAL;
     if (!(K == 1 || K == 2 || K == 4 || K == 8 || K == 16)) return OR_EINVAL;
     if (Z == 0 || Z % (OR_LANES * K) != 0) return OR_EINVAL;
     if (!esc_enabled && n_esc) return OR_EINVAL;
+    uint64_t n = rows * cols;
+    uint64_t n_chunks = (n + Z - 1) / Z;
+    uint64_t n_tab = seg ? (n_chunks + seg - 1) / seg : 1;
     uint32_t cum[257];
     uint8_t s2s[4096];
     uint32_t code[256];
-    if (codec == OR_CODEC_RANS ? !make_tables(table, cum, s2s) : !or_huff_codes(table, code))
-        return OR_EINVAL;
-    uint64_t n = rows * cols;
+    for (uint64_t g = 0; g < n_tab; g++) {
+        const uint16_t *table = tables + 256 * g;
+        if (codec == OR_CODEC_RANS ? !make_tables(table, cum, s2s) : !or_huff_codes(table, code))
+            return OR_EINVAL;
+    }
     for (uint64_t i = 0; i < n; i++)
-        if (table[sym[i]] == 0) return OR_EINVAL;
+        if (tables[256 * (seg ? (i / Z) / seg : 0) + sym[i]] == 0) return OR_EINVAL;
     for (uint64_t e = 0; e < n_esc; e++) {
         if (esc_idx[e] >= n || (e > 0 && esc_idx[e] <= esc_idx[e - 1])) return OR_EINVAL;
         if (sym[esc_idx[e]] != esc_code) return OR_EINVAL;
@@ -663,7 +692,6 @@ int or_encode_codec(uint32_t codec, uint32_t dtype, uint64_t rows, uint64_t cols
         if (cnt != n_esc) return OR_EINVAL;
     }
 
-    uint64_t n_chunks = (n + Z - 1) / Z;
     uint64_t n_states = codec == OR_CODEC_RANS ? n_chunks * OR_LANES : 0;
     uint32_t *states = malloc((n_states ? n_states : 1) * sizeof(uint32_t));
     uint64_t *wcount = malloc(n_chunks * sizeof(uint64_t));
@@ -678,10 +706,13 @@ int or_encode_codec(uint32_t codec, uint32_t dtype, uint64_t rows, uint64_t cols
         uint64_t p0 = k * Z;
         uint64_t nk = (n - p0 < Z) ? n - p0 : Z;
         wstart_unpadded[k] = used;
-        if (codec == OR_CODEC_RANS)
+        const uint16_t *table = tables + 256 * (seg ? k / seg : 0);
+        if (codec == OR_CODEC_RANS) {
+            make_tables(table, cum, s2s);
             wcount[k] = encode_chunk(sym + p0, nk, K, table, cum, states + k * OR_LANES, cw + used);
-        else
+        } else {
             wcount[k] = huff_encode_chunk(sym + p0, nk, K, table, code, cw + used);
+        }
         if (wcount[k] == UINT64_MAX) {
             free(states); free(wcount); free(cw); free(wstart_unpadded);
             return OR_ENOMEM;
@@ -693,7 +724,7 @@ int or_encode_codec(uint32_t codec, uint32_t dtype, uint64_t rows, uint64_t cols
     or_hdr h;
     memset(&h, 0, sizeof h);
     h.off_freq = OR_HDR_BYTES;
-    h.off_scales = align_up(h.off_freq + 512, OR_ALIGN);
+    h.off_scales = align_up(h.off_freq + 512 * n_tab, OR_ALIGN);
     h.off_dir = align_up(h.off_scales + rows * 4, OR_ALIGN);
     h.off_states = align_up(h.off_dir + n_chunks * 16, OR_ALIGN);
     h.off_words = align_up(h.off_states + n_states * 4, OR_ALIGN);
@@ -709,7 +740,7 @@ int or_encode_codec(uint32_t codec, uint32_t dtype, uint64_t rows, uint64_t cols
     put_u32(buf + 0, OR_MAGIC);
     put_u16(buf + 4, OR_VERSION);
     buf[6] = (uint8_t)dtype;
-    buf[7] = esc_enabled ? OR_FLAG_ESC : 0;
+    buf[7] = (esc_enabled ? OR_FLAG_ESC : 0) | (seg ? OR_FLAG_SEG : 0);
     put_u64(buf + 8, rows);
     put_u64(buf + 16, cols);
     put_u64(buf + 24, n);
@@ -730,8 +761,9 @@ int or_encode_codec(uint32_t codec, uint32_t dtype, uint64_t rows, uint64_t cols
     put_u64(buf + 128, h.off_esc_val);
     put_u64(buf + 136, h.total);
     put_u32(buf + 144, codec);
+    put_u32(buf + 148, seg);
 
-    for (int s = 0; s < 256; s++) put_u16(buf + h.off_freq + 2 * s, table[s]);
+    for (uint64_t i = 0; i < 256 * n_tab; i++) put_u16(buf + h.off_freq + 2 * i, tables[i]);
     for (uint64_t r = 0; r < rows; r++) {
         uint32_t b;
         memcpy(&b, &scales[r], 4);
@@ -794,6 +826,9 @@ static int parse(const uint8_t *b, uint64_t len, or_hdr *h) {
     h->off_esc_val = get_u64(b + 128);
     h->total = get_u64(b + 136);
     h->codec = get_u32(b + 144);
+    h->seg = get_u32(b + 148);
+    if (((h->flags & OR_FLAG_SEG) != 0) != (h->seg != 0)) return OR_ECORRUPT;
+    if (h->seg && (h->seg % 8 || h->codec != OR_CODEC_RANS)) return OR_ECORRUPT;
     if (h->codec != OR_CODEC_RANS && h->codec != OR_CODEC_HUFF) return OR_ECORRUPT;
     if (h->dtype != OR_DTYPE_INT8 && h->dtype != OR_DTYPE_E4M3) return OR_ECORRUPT;
     if (!(h->K == 1 || h->K == 2 || h->K == 4 || h->K == 8 || h->K == 16)) return OR_ECORRUPT;
@@ -801,7 +836,8 @@ static int parse(const uint8_t *b, uint64_t len, or_hdr *h) {
     if (h->rows == 0 || h->cols == 0 || h->n / h->rows != h->cols || h->n % h->rows) return OR_ECORRUPT;
     if (h->n_chunks != (h->n + h->Z - 1) / h->Z) return OR_ECORRUPT;
     if (h->total > len) return OR_ECORRUPT;
-    if (h->off_freq + 512 > h->total || h->off_scales + 4 * h->rows > h->total ||
+    if (h->off_freq + 512 * (h->seg ? (h->n_chunks + h->seg - 1) / h->seg : 1) > h->total ||
+        h->off_scales + 4 * h->rows > h->total ||
         h->off_dir + 16 * h->n_chunks > h->total ||
         h->off_states + (h->codec == OR_CODEC_RANS ? 4 * OR_LANES * h->n_chunks : 0) > h->total ||
         h->off_words + 2 * h->n_words > h->total || h->off_esc_idx + 8 * h->n_esc > h->total ||
@@ -864,7 +900,25 @@ static uint32_t decode_range(or_job *jb) {
         tmp = malloc(h->Z);
         if (!tmp) return OR_WORD_OVERRUN;
     }
+    /* adaptive tables: the segment's own table (rebuilt when the segment changes) */
+    uint16_t sfreq[256];
+    uint32_t scum[257];
+    uint8_t ss2s[4096];
+    uint64_t cur_seg = UINT64_MAX;
     for (uint64_t k = jb->k_lo; k < jb->k_hi; k++) {
+        const uint16_t *freq = jb->freq;
+        const uint32_t *cum = jb->cum;
+        const uint8_t *s2s = jb->s2s;
+        if (h->seg) {
+            if (k / h->seg != cur_seg) {
+                cur_seg = k / h->seg;
+                for (int t = 0; t < 256; t++) sfreq[t] = get_u16(b + h->off_freq + 512 * cur_seg + 2 * t);
+                make_tables(sfreq, scum, ss2s); /* validated by or_decode_chunks */
+            }
+            freq = sfreq;
+            cum = scum;
+            s2s = ss2s;
+        }
         uint64_t p0 = k * h->Z;
         uint64_t nk = (h->n - p0 < h->Z) ? h->n - p0 : h->Z;
         uint64_t ws = get_u64(b + h->off_dir + 16 * k);
@@ -873,7 +927,7 @@ static uint32_t decode_range(or_job *jb) {
         uint8_t *dst = jb->sym_out ? jb->sym_out + p0 : tmp;
         if (h->codec == OR_CODEC_RANS)
             flags |= decode_chunk(b + h->off_words + 2 * ws, wc, b + h->off_states + 4 * OR_LANES * k,
-                                  nk, h->K, jb->freq, jb->cum, jb->s2s, dst);
+                                  nk, h->K, freq, cum, s2s, dst);
         else
             flags |= huff_decode_chunk(b + h->off_words + 2 * ws, wc, nk, h->K, jb->canon, dst);
         if (jb->bf16_out) {
@@ -919,6 +973,15 @@ int64_t or_decode_chunks(const uint8_t *buf, uint64_t len, uint64_t k_lo, uint64
     or_canon canon;
     if (h.codec == OR_CODEC_RANS ? !make_tables(freq, cum, s2s) : !huff_canon(freq, &canon))
         return OR_ECORRUPT;
+    if (h.seg) {
+        uint16_t f2[256];
+        uint32_t c2[257];
+        uint8_t s2[4096];
+        for (uint64_t g = 0; g < (h.n_chunks + h.seg - 1) / h.seg; g++) {
+            for (int t = 0; t < 256; t++) f2[t] = get_u16(buf + h.off_freq + 512 * g + 2 * t);
+            if (!make_tables(f2, c2, s2)) return OR_ECORRUPT;
+        }
+    }
     if (nthreads < 1) nthreads = 1;
     uint64_t nk = k_hi - k_lo;
     if (nthreads > nk) nthreads = nk ? (uint32_t)nk : 1;
@@ -951,14 +1014,14 @@ int64_t or_decode_dequant(const uint8_t *buf, uint64_t len, uint16_t *bf16_out) 
 
 /* Header fields for the Python side: fills v[0..16) with dtype, flags, rows,
  * cols, n, Z, K, n_chunks, n_esc, esc_code, n_words, off_freq, off_scales,
- * off_dir, off_states, off_words; v[16..20) = off_esc_idx, off_esc_val, total, codec. */
-int or_header_fields(const uint8_t *buf, uint64_t len, uint64_t v[20]) {
+ * off_dir, off_states, off_words; v[16..21) = off_esc_idx, off_esc_val, total, codec, seg. */
+int or_header_fields(const uint8_t *buf, uint64_t len, uint64_t v[21]) {
     or_hdr h;
     int st = parse(buf, len, &h);
     if (st) return st;
-    uint64_t f[20] = {h.dtype, h.flags, h.rows, h.cols, h.n, h.Z, h.K, h.n_chunks, h.n_esc,
+    uint64_t f[21] = {h.dtype, h.flags, h.rows, h.cols, h.n, h.Z, h.K, h.n_chunks, h.n_esc,
                       h.esc_code, h.n_words, h.off_freq, h.off_scales, h.off_dir, h.off_states,
-                      h.off_words, h.off_esc_idx, h.off_esc_val, h.total, h.codec};
+                      h.off_words, h.off_esc_idx, h.off_esc_val, h.total, h.codec, h.seg};
     memcpy(v, f, sizeof f);
     return OR_OK;
 }

@@ -75,7 +75,8 @@ struct TArgs {
     uint64_t off_scales, off_dir, off_states, off_words, off_esc_idx, off_esc_val, off_freq;
     uint32_t Z, dtype, mode, const_sym;
     uint32_t is_const, wg_begin;
-    uint32_t codec, pad;  // entropy coder: eqfmt::kCodecRans or kCodecHuffman
+    uint32_t codec;       // entropy coder: eqfmt::kCodecRans or kCodecHuffman
+    uint32_t seg;         // adaptive tables: chunks per table (a multiple of kWaves), 0 = one table
     const uint16_t *x;  // fused GEMV: the tensor's bf16 input vector [cols]
     float *y;           // fused GEMV: its fp32 output [rows]
 };
@@ -190,8 +191,7 @@ __device__ __forceinline__ void raise_flag(uint32_t *status, uint32_t bits, uint
 // Slot table of the tensor: for every slot in [0, 4096) the byte s with
 // cum[s] <= slot < cum[s] + f[s], packed as s | f << 8 | (slot - cum[s]) << 20
 // (f <= 4095 here; a one-symbol tensor never builds a table).
-__device__ __forceinline__ void build_lut(const TArgs &T, LutEnt *lut, uint32_t *cum) {
-    const uint16_t *freq = reinterpret_cast<const uint16_t *>(T.base + T.off_freq);
+__device__ __forceinline__ void build_lut(const uint16_t *freq, LutEnt *lut, uint32_t *cum) {
     const uint32_t tid = threadIdx.x;
     if (tid < 64) {
         uint32_t f[4];
@@ -850,7 +850,12 @@ __global__ void __launch_bounds__(kThreads) k_decode(LArgs a) {
             build_lut_huff(reinterpret_cast<const uint16_t *>(T.base + T.off_freq),
                            reinterpret_cast<uint32_t *>(lut), reinterpret_cast<uint32_t *>(&rings[0][0]));
         else
-            build_lut(T, lut, reinterpret_cast<uint32_t *>(&rings[0][0]));
+            // the workgroup's chunks share one table (with adaptive tables the
+            // segment size is a multiple of the waves per workgroup)
+            build_lut(reinterpret_cast<const uint16_t *>(
+                          T.base + T.off_freq +
+                          (T.seg ? 512ull * (((uint64_t)(wg - T.wg_begin) * kWaves) / T.seg) : 0ull)),
+                      lut, reinterpret_cast<uint32_t *>(&rings[0][0]));
     }
     if (chunk >= T.n_chunks) return;
     if (is_const) {
@@ -982,7 +987,9 @@ bool header_ok(const eq_header &h) {
     if (h.rows == 0 || h.cols == 0 || h.rows * h.cols != h.n) return false;
     if (h.n_chunks != (h.n + h.chunk_symbols - 1) / h.chunk_symbols) return false;
     if (h.codec != eqfmt::kCodecRans && h.codec != eqfmt::kCodecHuffman) return false;
-    const eqfmt::Sections s = eqfmt::layout(h.rows, h.n_chunks, h.n_words, h.n_esc, h.codec);
+    if (h.seg_chunks && (h.seg_chunks % 8 || h.codec != eqfmt::kCodecRans)) return false;
+    const eqfmt::Sections s = eqfmt::layout(h.rows, h.n_chunks, h.n_words, h.n_esc, h.codec,
+                                            eqfmt::n_tables(h.n_chunks, h.seg_chunks));
     return s.freq == h.off_freq && s.scales == h.off_scales && s.dir == h.off_dir &&
            s.states == h.off_states && s.words == h.off_words && s.esc_idx == h.off_esc_idx &&
            s.esc_val == h.off_esc_val && s.total == h.total_bytes;
@@ -1032,7 +1039,8 @@ eq_status launch_block(const eq_block *b, void *out, const uint16_t *const *x, f
             t.Z = h.chunk_symbols;
             t.dtype = h.dtype;
             t.codec = h.codec;
-            t.pad = 0;
+            t.seg = h.seg_chunks;
+            if (t.seg % kWaves) return EQ_EUNSUPPORTED;
             t.is_const = 0;
             t.const_sym = 0;
             if (h.single_symbol >= 0) {

@@ -416,7 +416,7 @@ eq_status eq_encode_device(const eq_tensor_desc *d, const uint8_t *d_symbols, co
                            uint64_t *d_out_len, uint32_t *d_status, void *stream) {
     if (!d || !d_symbols || !d_scales || !d_workspace || !d_out) return EQ_EINVAL;
     if (n_esc && (!d_esc_idx || !d_esc_bf16)) return EQ_EINVAL;
-    if (d->codec != kCodecRans) return EQ_EUNSUPPORTED;
+    if (d->codec != kCodecRans || d->seg_chunks) return EQ_EUNSUPPORTED;
     if (d->dtype != EQ_DTYPE_INT8 && d->dtype != EQ_DTYPE_E4M3) return EQ_EINVAL;
     if (d->rows == 0 || d->cols == 0 || d->cols > (1ull << 40) / d->rows) return EQ_EINVAL;
     if (!valid_lane_run(d->lane_run)) return EQ_EINVAL;

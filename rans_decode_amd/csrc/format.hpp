@@ -27,8 +27,9 @@ enum HeaderField : uint32_t {
     H_CHUNK = 32, H_LANE_RUN = 36, H_LANES = 40, H_PROB_BITS = 44, H_NCHUNKS = 48, H_NESC = 56,
     H_ESC_CODE = 64, H_NWORDS = 72, H_OFF_FREQ = 80, H_OFF_SCALES = 88, H_OFF_DIR = 96,
     H_OFF_STATES = 104, H_OFF_WORDS = 112, H_OFF_ESC_IDX = 120, H_OFF_ESC_VAL = 128, H_TOTAL = 136,
-    H_CODEC = 144,
+    H_CODEC = 144, H_SEG = 148,
 };
+constexpr uint8_t kFlagEsc = 1, kFlagSeg = 2;
 
 constexpr uint64_t round_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 
@@ -40,7 +41,7 @@ struct Sections {
 // on a 256-byte boundary right after the previous one (the Huffman codec
 // stores no lane states).
 inline Sections layout(uint64_t rows, uint64_t n_chunks, uint64_t n_words, uint64_t n_esc,
-                       uint32_t codec = kCodecRans) {
+                       uint32_t codec = kCodecRans, uint64_t n_tables = 1) {
     Sections s{};
     uint64_t at = kHeaderBytes;
     auto place = [&](uint64_t bytes) {
@@ -48,7 +49,7 @@ inline Sections layout(uint64_t rows, uint64_t n_chunks, uint64_t n_words, uint6
         at = start + bytes;
         return start;
     };
-    s.freq = place(256 * 2);
+    s.freq = place(256 * 2 * n_tables);
     s.scales = place(rows * 4);
     s.dir = place(n_chunks * kDirEntryBytes);
     s.states = place(codec == kCodecRans ? n_chunks * kLanes * 4 : 0);
@@ -58,6 +59,9 @@ inline Sections layout(uint64_t rows, uint64_t n_chunks, uint64_t n_words, uint6
     s.total = round_up(at, kSectionAlign);
     return s;
 }
+
+// Frequency tables of a container: one, or one per segment of seg chunks.
+inline uint64_t n_tables(uint64_t n_chunks, uint32_t seg) { return seg ? (n_chunks + seg - 1) / seg : 1; }
 
 inline bool valid_lane_run(uint32_t k) { return k == 1 || k == 2 || k == 4 || k == 8 || k == 16; }
 

@@ -331,7 +331,10 @@ eq_status eq_build_tables(const uint8_t *symbols, uint64_t n, eq_tables *out) {
 eq_status eq_encode_host(const eq_tables *t, const eq_tensor_desc *d, const uint8_t *symbols,
                          const float *scales, const uint64_t *esc_idx, const uint16_t *esc_bf16,
                          uint64_t n_esc, void *out, uint64_t cap, uint64_t *out_len) {
-    if (!t || !d || !symbols || !scales || !out_len) return EQ_EINVAL;
+    if (!d || !symbols || !scales || !out_len) return EQ_EINVAL;
+    const uint32_t seg = d->seg_chunks;
+    if ((!t && !seg) || d->reserved) return EQ_EINVAL;
+    if (seg && (seg % 8 || d->codec != kCodecRans)) return EQ_EINVAL;
     if (n_esc && (!esc_idx || !esc_bf16)) return EQ_EINVAL;
     if (d->dtype != EQ_DTYPE_INT8 && d->dtype != EQ_DTYPE_E4M3) return EQ_EINVAL;
     if (d->rows == 0 || d->cols == 0 || d->cols > (1ull << 40) / d->rows) return EQ_EINVAL;
@@ -347,7 +350,7 @@ eq_status eq_encode_host(const eq_tables *t, const eq_tensor_desc *d, const uint
     uint16_t table[256];
     if (huff) {
         if (!huffman_lengths(t->counts, table)) return EQ_EINVAL;
-    } else {
+    } else if (!seg) {
         uint32_t fsum = 0;
         for (int s = 0; s < 256; ++s) {
             fsum += t->freq[s];
@@ -375,7 +378,7 @@ eq_status eq_encode_host(const eq_tables *t, const eq_tensor_desc *d, const uint
         bool b = false;
         for (uint64_t k = lo; k < hi; ++k) {
             const uint8_t c = symbols[k];
-            b |= table[c] == 0;
+            b |= !seg && table[c] == 0;
             const bool is_esc = d->esc_enabled && c == d->esc_code;
             seen += is_esc;
             b |= d->dtype == EQ_DTYPE_E4M3 && is_e4m3_nan(c) && !is_esc;
@@ -390,24 +393,49 @@ eq_status eq_encode_host(const eq_tables *t, const eq_tensor_desc *d, const uint
     }
     if (esc_total != n_esc) return EQ_EINVAL;
 
-    SymInfo tab[256];
+    const uint64_t n_chunks = (n + Z - 1) / Z;
+    const uint64_t n_tab = n_tables(n_chunks, seg);
+    // the stored tables: one (the caller's, or the Huffman lengths), or with
+    // adaptive tables each segment's own quantised counts
+    std::vector<uint16_t> tables(256 * n_tab);
+    if (seg) {
+        std::vector<uint8_t> bad_seg(n_tab, 0);
+        parallel_for(n_tab, [&](uint64_t g) {
+            uint64_t counts[256] = {};
+            const uint64_t lo = g * seg * Z, hi = std::min(n, (g + 1) * seg * Z);
+            for (uint64_t i = lo; i < hi; ++i) ++counts[symbols[i]];
+            bad_seg[g] = quantise(counts, hi - lo, &tables[256 * g]) != EQ_OK;
+        });
+        for (uint64_t g = 0; g < n_tab; ++g)
+            if (bad_seg[g]) return EQ_EINVAL;
+    } else {
+        std::copy(table, table + 256, tables.begin());
+    }
+    std::vector<SymInfo> tab(huff ? 0 : 256 * n_tab);
     uint32_t hcode[256];
     if (huff) {
         huffman_codes(table, hcode);
     } else {
-        for (int s = 0; s < 256; ++s) {
-            tab[s].freq = t->freq[s] ? t->freq[s] : 1;
-            tab[s].start = t->cum[s];
-            tab[s].renorm_at = (uint64_t)t->freq[s] << 20;
+        for (uint64_t g = 0; g < n_tab; ++g) {
+            uint32_t c = 0;
+            for (int s = 0; s < 256; ++s) {
+                const uint16_t f = tables[256 * g + s];
+                SymInfo &si = tab[256 * g + s];
+                si.freq = f ? f : 1;
+                si.start = c;
+                si.renorm_at = (uint64_t)f << 20;
+                c += f;
+            }
         }
-        uint32_t c = 0;  // cum must match freq
-        for (int s = 0; s < 256; ++s) {
-            if (t->cum[s] != c) return EQ_EINVAL;
-            c += t->freq[s];
+        if (!seg) {
+            uint32_t c = 0;  // the caller's cum must match its freq
+            for (int s = 0; s < 256; ++s) {
+                if (t->cum[s] != c) return EQ_EINVAL;
+                c += t->freq[s];
+            }
         }
     }
 
-    const uint64_t n_chunks = (n + Z - 1) / Z;
     std::unique_ptr<uint16_t[]> scratch(new (std::nothrow) uint16_t[n]);
     std::unique_ptr<uint32_t[]> states(new (std::nothrow) uint32_t[huff ? 1 : n_chunks * kLanes]);
     std::unique_ptr<uint64_t[]> wcount(new (std::nothrow) uint64_t[n_chunks]);
@@ -421,13 +449,13 @@ eq_status eq_encode_host(const eq_tables *t, const eq_tensor_desc *d, const uint
         if (huff)
             wcount[k] = huffman_encode_chunk(symbols + p0, nk, K, table, hcode, scratch.get() + p0);
         else
-            wcount[k] = encode_chunk(symbols + p0, nk, K, tab, &states[k * kLanes],
-                                     scratch.get() + p0 + nk);
+            wcount[k] = encode_chunk(symbols + p0, nk, K, &tab[256 * (seg ? k / seg : 0)],
+                                     &states[k * kLanes], scratch.get() + p0 + nk);
     });
 
     uint64_t n_words = 0;
     for (uint64_t k = 0; k < n_chunks; ++k) n_words += round_up(wcount[k], kWordPad);
-    const Sections sec = layout(d->rows, n_chunks, n_words, n_esc, d->codec);
+    const Sections sec = layout(d->rows, n_chunks, n_words, n_esc, d->codec, n_tab);
     *out_len = sec.total;
     if (!out || cap < sec.total) return EQ_ERANGE;
 
@@ -436,7 +464,7 @@ eq_status eq_encode_host(const eq_tables *t, const eq_tensor_desc *d, const uint
     wr32(b + H_MAGIC, kMagic);
     wr16(b + H_VERSION, kVersion);
     b[H_DTYPE] = (uint8_t)d->dtype;
-    b[H_FLAGS] = d->esc_enabled ? 1 : 0;
+    b[H_FLAGS] = (d->esc_enabled ? kFlagEsc : 0) | (seg ? kFlagSeg : 0);
     wr64(b + H_ROWS, d->rows);
     wr64(b + H_COLS, d->cols);
     wr64(b + H_N, n);
@@ -457,8 +485,9 @@ eq_status eq_encode_host(const eq_tables *t, const eq_tensor_desc *d, const uint
     };
     zero_to(H_CODEC, sec.freq);
     wr32(b + H_CODEC, d->codec);
+    wr32(b + H_SEG, seg);
     zero_to(sec.freq, sec.total);  // gaps and padding words are zero
-    for (int s = 0; s < 256; ++s) wr16(b + sec.freq + 2 * s, table[s]);
+    for (uint64_t i = 0; i < 256 * n_tab; ++i) wr16(b + sec.freq + 2 * i, tables[i]);
     std::memcpy(b + sec.scales, scales, d->rows * 4);
 
     std::vector<uint64_t> first(n_chunks);
@@ -509,12 +538,16 @@ eq_status eq_parse_header(const void *bytes, uint64_t len, eq_header *out) {
     h.total_bytes = rd64(b + H_TOTAL);
     h.single_symbol = -1;
     h.codec = rd32(b + H_CODEC);
-    h.reserved = 0;
+    h.seg_chunks = rd32(b + H_SEG);
     if (h.codec != kCodecRans && h.codec != kCodecHuffman) return EQ_ECORRUPT;
     const bool huff = h.codec == kCodecHuffman;
+    const uint32_t seg = h.seg_chunks;
+    if (((h.flags & kFlagSeg) != 0) != (seg != 0)) return EQ_ECORRUPT;
+    if (seg && (seg % 8 || huff)) return EQ_ECORRUPT;
 
     if (h.dtype != EQ_DTYPE_INT8 && h.dtype != EQ_DTYPE_E4M3) return EQ_ECORRUPT;
-    if (h.flags > 1 || (!(h.flags & 1) && (h.n_esc || h.esc_code))) return EQ_ECORRUPT;
+    if (h.flags > (kFlagEsc | kFlagSeg) || (!(h.flags & kFlagEsc) && (h.n_esc || h.esc_code)))
+        return EQ_ECORRUPT;
     if (rd32(b + H_LANES) != kLanes || rd32(b + H_PROB_BITS) != (huff ? kHuffMaxLen : kProbBits))
         return EQ_ECORRUPT;
     if (!valid_lane_run(h.lane_run)) return EQ_ECORRUPT;
@@ -527,9 +560,10 @@ eq_status eq_parse_header(const void *bytes, uint64_t len, eq_header *out) {
     if (h.n_esc > h.n || h.n_words > h.n + 8 * h.n_chunks) return EQ_ECORRUPT;
     for (size_t i = 65; i < 72; ++i)
         if (b[i]) return EQ_ECORRUPT;
-    for (size_t i = H_CODEC + 4; i < kHeaderBytes; ++i)
+    for (size_t i = H_SEG + 4; i < kHeaderBytes; ++i)
         if (b[i]) return EQ_ECORRUPT;
-    const Sections sec = layout(h.rows, h.n_chunks, h.n_words, h.n_esc, h.codec);
+    const uint64_t n_tab = n_tables(h.n_chunks, seg);
+    const Sections sec = layout(h.rows, h.n_chunks, h.n_words, h.n_esc, h.codec, n_tab);
     if (h.off_freq != sec.freq || h.off_scales != sec.scales || h.off_dir != sec.dir ||
         h.off_states != sec.states || h.off_words != sec.words || h.off_esc_idx != sec.esc_idx ||
         h.off_esc_val != sec.esc_val || h.total_bytes != sec.total)
@@ -543,13 +577,15 @@ eq_status eq_parse_header(const void *bytes, uint64_t len, eq_header *out) {
         if (!huffman_table_ok(table, &lone)) return EQ_ECORRUPT;
         h.single_symbol = lone;
     } else {
-        uint32_t fsum = 0;
-        for (int s = 0; s < 256; ++s) {
-            const uint16_t f = rd16(b + h.off_freq + 2 * s);
-            fsum += f;
-            if (f == kProbScale) h.single_symbol = s;
+        for (uint64_t g = 0; g < n_tab; ++g) {
+            uint32_t fsum = 0;
+            for (int s = 0; s < 256; ++s) {
+                const uint16_t f = rd16(b + h.off_freq + 512 * g + 2 * s);
+                fsum += f;
+                if (f == kProbScale && !seg) h.single_symbol = s;
+            }
+            if (fsum != kProbScale) return EQ_ECORRUPT;
         }
-        if (fsum != kProbScale) return EQ_ECORRUPT;
     }
 
     // directory: consecutive padded word ranges covering exactly n_words

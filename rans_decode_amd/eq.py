@@ -42,14 +42,14 @@ class eq_tables(ctypes.Structure):
 class eq_tensor_desc(ctypes.Structure):
     _fields_ = [("dtype", _u32), ("lane_run", _u32), ("rows", _u64), ("cols", _u64),
                 ("chunk_symbols", _u32), ("esc_enabled", _u32), ("esc_code", _u32),
-                ("codec", _u32)]
+                ("codec", _u32), ("seg_chunks", _u32), ("reserved", _u32)]
 
 
 class eq_header(ctypes.Structure):
     _fields_ = [("dtype", _u32), ("flags", _u32), ("chunk_symbols", _u32), ("lane_run", _u32),
                 ("rows", _u64), ("cols", _u64), ("n", _u64), ("n_chunks", _u64), ("n_esc", _u64),
                 ("n_words", _u64), ("esc_code", _u32), ("single_symbol", _i32),
-                ("codec", _u32), ("reserved", _u32), ("off_freq", _u64), ("off_scales", _u64), ("off_dir", _u64), ("off_states", _u64),
+                ("codec", _u32), ("seg_chunks", _u32), ("off_freq", _u64), ("off_scales", _u64), ("off_dir", _u64), ("off_states", _u64),
                 ("off_words", _u64), ("off_esc_idx", _u64), ("off_esc_val", _u64),
                 ("total_bytes", _u64)]
 
@@ -157,13 +157,14 @@ def eq_encode_host(tables: eq_tables, desc: eq_tensor_desc, symbols: np.ndarray,
     if symbols.size != desc.rows * desc.cols or scales.size != desc.rows or esc_idx.size != esc_val.size:
         raise ValueError("symbols / scales / escape arrays do not match the descriptor")
     need = _u64(0)
-    args = (ctypes.byref(tables), ctypes.byref(desc), symbols.ctypes.data, scales.ctypes.data,
+    args = (ctypes.byref(tables) if tables is not None else None, ctypes.byref(desc), symbols.ctypes.data, scales.ctypes.data,
             esc_idx.ctypes.data if esc_idx.size else None,
             esc_val.ctypes.data if esc_val.size else None, esc_idx.size)
     # upper bound of the container size (at most one word per symbol), then
     # one encoding pass; EQ_ERANGE reports the exact size if the bound is short
     n_chunks = -(-symbols.size // desc.chunk_symbols) if desc.chunk_symbols else 1
-    bound = (256 + 512 + 4 * desc.rows + 16 * n_chunks + 256 * n_chunks
+    n_tab = -(-n_chunks // desc.seg_chunks) if desc.seg_chunks else 1
+    bound = (256 + 512 * n_tab + 4 * desc.rows + 16 * n_chunks + 256 * n_chunks
              + 2 * (symbols.size + 8 * n_chunks) + 10 * esc_idx.size + 8 * 256)
     buf = np.empty(bound, dtype=np.uint8)
     st = _lib.eq_encode_host(*args, buf.ctypes.data, buf.size, ctypes.byref(need))
@@ -176,11 +177,12 @@ def eq_encode_host(tables: eq_tables, desc: eq_tensor_desc, symbols: np.ndarray,
 
 def encode_host(tables: eq_tables, dtype: int, rows: int, cols: int, symbols: np.ndarray,
                 scales: np.ndarray, esc_idx=None, esc_val=None, esc_code: int = 0,
-                chunk_symbols: int = 65536, lane_run: int = 8, codec: int = 0) -> np.ndarray:
+                chunk_symbols: int = 65536, lane_run: int = 8, codec: int = 0,
+                seg_chunks: int = 0) -> np.ndarray:
     n_esc = 0 if esc_idx is None else len(esc_idx)
     d = eq_tensor_desc(dtype=dtype, lane_run=lane_run, rows=rows, cols=cols,
                        chunk_symbols=chunk_symbols, esc_enabled=1 if n_esc or esc_code else 0,
-                       esc_code=esc_code, codec=codec)
+                       esc_code=esc_code, codec=codec, seg_chunks=seg_chunks)
     return eq_encode_host(tables, d, symbols, scales, esc_idx, esc_val)
 
 

@@ -360,3 +360,21 @@ def gemv_activation(cfg: int, layer: int, t: int, cols: int) -> np.ndarray:
     r = np.sqrt(-2.0 * np.log1p(-u1))
     z = np.concatenate([r * np.cos(2 * np.pi * u2), r * np.sin(2 * np.pi * u2)])[:cols]
     return z.astype(np.float32)
+
+
+DRIFT_BITS = (0.8, 2.1, 3.2, 1.4)
+
+
+def drift_tensor(rows: int, cols: int, bands: int = 16, bits=DRIFT_BITS, seed: int = 0) -> Tensor:
+    """Int8 tensor whose statistics drift along the rows: the rows are cut into
+    `bands` equal bands, band b drawn i.i.d. from the discrete Laplace whose
+    entropy is bits[b % len(bits)]. Per-row scales as for the configs. Input
+    for the adaptive-table comparison (one table vs one table per segment)."""
+    spec = TensorSpec("drift", rows, cols, DTYPE_INT8, 0.0)
+    sym = np.empty(rows * cols, np.uint8)
+    edges = [rows * b // bands for b in range(bands + 1)]
+    for b in range(bands):
+        lo, hi = edges[b] * cols, edges[b + 1] * cols
+        cat = laplace_table(theta_for_entropy(bits[b % len(bits)]))
+        sym[lo:hi] = sample(cat, stream_key(99, seed, b, PURPOSE_SYMBOLS), 0, hi - lo)
+    return Tensor(spec, sym, scales_for(4, seed, 4, rows))

@@ -333,3 +333,53 @@ def test_huffman_lone_symbol_and_parse_checks():
         eq.encode_host(tab, 1, 9, 1000, sym, np.ones(9, np.float32), codec=eq.EQ_CODEC_HUFFMAN)
     with pytest.raises(eq.EqError):
         eq.encode_host(eq.build_tables(sym), 1, 9, 1000, sym, np.ones(9, np.float32), codec=5)
+
+
+# --- adaptive (per-segment) frequency tables
+
+def _seg_tables_oracle(sym, Z, seg):
+    n_chunks = -(-sym.size // Z)
+    n_seg = -(-n_chunks // seg)
+    return np.stack([oracle.build_freq(sym[g * seg * Z:(g + 1) * seg * Z]) for g in range(n_seg)])
+
+
+def test_segment_tables_byte_equal_to_oracle():
+    rng = np.random.default_rng(29)
+    for it in range(120):
+        K = int(rng.choice([1, 2, 4, 8, 16]))
+        Z = 64 * K * int(rng.integers(1, 4))
+        seg = 8 * int(rng.integers(1, 4))
+        n = int(rng.integers(1, Z * seg * 3))
+        drift = np.linspace(0, int(rng.integers(0, 60)), n).astype(np.int64)
+        sym = ((rng.geometric(float(rng.uniform(0.2, 0.8)), n) + drift) % 256).astype(np.uint8)
+        divs = [d for d in range(1, min(n, 32) + 1) if n % d == 0]
+        rows = int(rng.choice(divs))
+        scales = rng.uniform(-1, 1, rows).astype(np.float32)
+        ours = eq.encode_host(None, 1, rows, n // rows, sym, scales, chunk_symbols=Z, lane_run=K,
+                              seg_chunks=seg)
+        ref = oracle.encode(1, rows, n // rows, sym, scales, _seg_tables_oracle(sym, Z, seg), Z, K,
+                            seg_chunks=seg)
+        assert np.array_equal(ours, ref), (it, K, Z, seg, n)
+        h = eq.parse_header(ours)
+        assert h.seg_chunks == seg and h.single_symbol == -1
+
+
+def test_segment_tables_parse_and_argument_checks():
+    rng = np.random.default_rng(4)
+    sym = rng.choice([0, 1, 2, 250], 64 * 1024, p=[0.6, 0.2, 0.15, 0.05]).astype(np.uint8)
+    c = eq.encode_host(None, 1, 64, 1024, sym, np.ones(64, np.float32), chunk_symbols=512, lane_run=8,
+                       seg_chunks=16)
+    h = eq.parse_header(c)
+    assert h.off_scales - h.off_freq == 512 * (-(-128 // 16))
+    for name, mutate in [("flag without size", lambda x: x.__setitem__(148, 0)),
+                         ("size not a multiple of 8", lambda x: x.__setitem__(148, 12)),
+                         ("second table sum", lambda x: x.__setitem__(h.off_freq + 512, x[h.off_freq + 512] ^ 1))]:
+        bad = c.copy()
+        mutate(bad)
+        with pytest.raises(eq.EqError) as ei:
+            eq.parse_header(bad)
+        assert ei.value.status == eq.EQ_ECORRUPT, name
+    for seg, codec in [(4, 0), (8, eq.EQ_CODEC_HUFFMAN)]:
+        with pytest.raises(eq.EqError):
+            eq.encode_host(eq.build_tables(sym), 1, 64, 1024, sym, np.ones(64, np.float32),
+                           chunk_symbols=512, seg_chunks=seg, codec=codec)
