@@ -49,6 +49,9 @@ namespace {
 #ifndef EQ_LUT8
 #define EQ_LUT8 1
 #endif
+#ifndef EQ_RENORM_EXEC
+#define EQ_RENORM_EXEC 1
+#endif
 #ifndef EQ_NT_STORES
 #define EQ_NT_STORES 1
 #endif
@@ -397,10 +400,22 @@ struct Chunk {
         const uint32_t rank = __builtin_amdgcn_mbcnt_hi(
             (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
         const uint32_t w = ring[(ptr & (kRing - 1u)) + rank];
+        uint32_t b = x, nb = nbits;
+#if EQ_RENORM_EXEC
+        // under an exec mask of the refilling lanes (see the rANS step)
+        uint64_t saved;
+        asm volatile("s_and_saveexec_b64 %2, %3\n\t"
+                     "v_lshl_or_b32 %0, %4, %1, %0\n\t"
+                     "v_add_u32 %1, 16, %1\n\t"
+                     "s_mov_b64 exec, %2"
+                     : "+v"(b), "+v"(nb), "=&s"(saved)
+                     : "s"(m), "v"(w)
+                     : "scc");
+#else
         const uint32_t merged = (w << nbits) | x;
-        uint32_t b, nb;
         asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(b) : "v"(x), "v"(merged), "s"(m));
         asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(nb) : "v"(nbits), "v"(nbits + 16u), "s"(m));
+#endif
         ptr += (uint32_t)__builtin_popcountll(m);
         const uint32_t e = tab[b & 4095u];
         const uint32_t bn = b >> (e & 31u);
@@ -430,11 +445,24 @@ struct Chunk {
         // every lane reads ring[ptr + rank] (always inside the staged window
         // plus its 64-word copy); only lanes that need a word keep it
         const uint32_t w = ring[(ptr & (kRing - 1u)) + rank];
+#if EQ_RENORM_EXEC
+        // merge under an exec mask of the renormalising lanes: one VALU
+        // instruction, the mask set and restored by the scalar unit (the
+        // VALU, not the SALU, is the saturated resource)
+        uint64_t saved;
+        asm volatile("s_and_saveexec_b64 %1, %2\n\t"
+                     "v_lshl_or_b32 %0, %0, 16, %3\n\t"
+                     "s_mov_b64 exec, %1"
+                     : "+v"(xn), "=&s"(saved)
+                     : "s"(m), "v"(w)
+                     : "scc");
+#else
         const uint32_t merged = (xn << 16) | w;
         uint32_t sel;
         // a VALU select on the ballot mask (keeps the ring read unconditional)
         asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(sel) : "v"(xn), "v"(merged), "s"(m));
         xn = sel;
+#endif
 #else
         if (need) xn = (xn << 16) | ring[(ptr & (kRing - 1u)) + rank];
 #endif
