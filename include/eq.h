@@ -276,7 +276,7 @@ eq_status eq_decode_gemv_bf16(const eq_block *b, const uint16_t *const *d_x, flo
  *    receiving the container size; may be NULL), d_status (device u32, caller
  *    zeroed, may be NULL: EQ_DEV_BAD_INPUT when a symbol, escape list or
  *    scale is invalid; the container is then unspecified).
- * Enqueues seven kernels on stream; never allocates or synchronises.
+ * Enqueues six kernels on stream; never allocates or synchronises.
  * Errors: EQ_EINVAL (arguments), EQ_ERANGE (workspace or cap too small),
  * EQ_EUNSUPPORTED (codec), EQ_EHIP (launch).
  */

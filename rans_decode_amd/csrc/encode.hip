@@ -10,20 +10,28 @@
 // this is the encode half of that, on the GPU (the scale optimisation before
 // it is not part of this library).
 //
-// Pipeline (one stream, seven launches, no host synchronisation):
-//   zero    workspace counters
-//   hist    per-workgroup LDS histograms -> 256 u64 counts
-//   check   super-weight list and scales (and copy the scales)
+// Pipeline (one stream, six launches, no host synchronisation):
+//   check   super-weight list and scales (and copy the scales); clear the
+//           workspace counters
+//   hist    per-workgroup LDS histograms (32 copies, one per LDS bank, so
+//           the few frequent codes of a low-entropy tensor do not serialise
+//           the atomics) -> 256 u64 counts (global atomics, nonzero
+//           counts only)
 //   quant   the quantiser (rule stated in include/eq.h) -> freq/cum, header,
 //           frequency section
 //   chunks  one wave per chunk: lanes walk the chunk's steps backwards; a lane
 //           whose state reached f * 2^20 emits its low 16 bits first; the
 //           words of one step take consecutive slots in ascending lane order
 //           (ballot + mbcnt), filled from the end of the chunk's scratch
-//           region, so they come out in the decoder's reading order
+//           region, so they come out in the decoder's reading order. Words
+//           collect in a per-wave LDS ring and leave in 1 KiB aligned blocks;
+//           the division by f is one binary64 fused multiply-add with the
+//           symbol's reciprocal (exact, see enc_div)
 //   scan    one workgroup: padded word counts -> directory, n_words, the
 //           offsets that depend on it, the total size
-//   copy    words to their final place, escape list, zero gaps
+//   copy    words to their final place (16-byte stores; the word offset
+//           inside the scratch is wave-uniform, so each lane realigns two
+//           aligned loads), escape list, zero gaps
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -38,14 +46,28 @@ using namespace eqfmt;
 constexpr int kEncWaves = 4;                   // chunks per workgroup
 constexpr int kEncThreads = 64 * kEncWaves;
 
+// Per-symbol encoder constants: the reciprocal of f for the division, f and
+// 4096 - f, the cumulative frequency.
+struct EncSym {
+    double rcp;    // 1 / f rounded to binary64 (0 for absent symbols)
+    uint32_t fg;   // 16 f (0xFFFF for f = 4096) | (4096 - f) << 16
+    uint32_t cum;
+};
+static_assert(sizeof(EncSym) == 16, "one 16-byte LDS read per step");
+
+constexpr uint32_t kEncRing = 2048;   // words of a wave's output ring
+constexpr uint32_t kHistMaxGrid = 1024;  // histogram workgroups at most (4 per CU)
+constexpr uint32_t kEncFlush = 512;   // words per ring flush (8 per lane)
+
 // Workspace layout (bytes from the start; all 256-byte aligned).
 struct WsLayout {
     uint64_t counts;   // 256 x u64
-    uint64_t table;    // 256 x u32: freq | cum << 16
+    uint64_t table;    // 256 x EncSym
     uint64_t misc;     // u64 n_words, u64 total
     uint64_t wstart;   // n_chunks x u32: first word of the chunk inside its scratch region
     uint64_t first;    // n_chunks x u64: first word in the container
-    uint64_t scratch;  // n x u16 (chunk k uses [k*Z, k*Z + nk))
+    uint64_t scratch;  // n + 16 x u16 (chunk k uses [k*Z, k*Z + nk); the tail chunk's
+                       // last aligned block and the copy's read-ahead go past n)
     uint64_t total;
 };
 
@@ -58,11 +80,11 @@ __host__ __device__ inline WsLayout ws_layout(uint64_t n, uint64_t n_chunks) {
         return start;
     };
     w.counts = place(256 * 8);
-    w.table = place(256 * 4);
+    w.table = place(256 * sizeof(EncSym));
     w.misc = place(16);
     w.wstart = place(n_chunks * 4);
     w.first = place(n_chunks * 8);
-    w.scratch = place(n * 2);
+    w.scratch = place((n + 16) * 2);
     w.total = round_up(at, 256);
     return w;
 }
@@ -91,46 +113,55 @@ __device__ inline T *at(uint8_t *base, uint64_t off) {
     return reinterpret_cast<T *>(base + off);
 }
 
-__global__ void k_enc_zero(EncArgs a) {
-    const uint32_t i = threadIdx.x;
-    if (i < 256) at<uint64_t>(a.ws, a.w.counts)[i] = 0;
-    if (i < 2) at<uint64_t>(a.ws, a.w.misc)[i] = 0;
-}
 
-// Histogram: each wave keeps its own 256 LDS counters (fewer collisions on
-// the few frequent codes), 16 symbols per thread per iteration.
+// Histogram: 32 copies of the 256 counters per workgroup, bin-major, copy =
+// lane mod 32, so the 32 lanes an LDS atomic serves at once hit 32 different
+// banks whatever their codes; 16 symbols per thread per iteration.
+constexpr uint32_t kHistCopies = 32;
+
 __global__ void __launch_bounds__(256) k_enc_hist(EncArgs a) {
-    __shared__ uint32_t h[4][256];
-    const uint32_t wave = threadIdx.x >> 6;
-    for (uint32_t i = threadIdx.x; i < 4 * 256; i += blockDim.x) (&h[0][0])[i] = 0;
+    __shared__ uint32_t h[256 * kHistCopies];
+    for (uint32_t i = threadIdx.x; i < 256 * kHistCopies; i += blockDim.x) h[i] = 0;
     __syncthreads();
+    const uint32_t c = threadIdx.x & (kHistCopies - 1u);
     const uint64_t n16 = a.n / 16;
     const uint4 *v = reinterpret_cast<const uint4 *>(a.sym);
     const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
-    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) {
-        const uint4 q = v[i];
-        const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
+    auto count4 = [&](uint32_t wd) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int b = 0; b < 4; ++b) atomicAdd(&h[wave][(wd[j] >> (8 * b)) & 0xFFu], 1u);
+        for (int b = 0; b < 4; ++b) atomicAdd(&h[((wd >> (8 * b)) & 0xFFu) * kHistCopies + c], 1u);
+    };
+    uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + stride < n16; i += 2 * stride) {  // two 16-byte loads in flight per thread
+        const uint4 q0 = v[i], q1 = v[i + stride];
+        count4(q0.x); count4(q0.y); count4(q0.z); count4(q0.w);
+        count4(q1.x); count4(q1.y); count4(q1.z); count4(q1.w);
     }
-    for (uint64_t i = n16 * 16 + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < a.n; i += stride)
-        atomicAdd(&h[wave][a.sym[i]], 1u);
+    if (i < n16) {
+        const uint4 q0 = v[i];
+        count4(q0.x); count4(q0.y); count4(q0.z); count4(q0.w);
+    }
+    for (uint64_t j = n16 * 16 + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; j < a.n; j += stride)
+        atomicAdd(&h[a.sym[j] * kHistCopies + c], 1u);
     __syncthreads();
     if (threadIdx.x < 256) {
         const uint32_t s = threadIdx.x;
-        const uint64_t c = (uint64_t)h[0][s] + h[1][s] + h[2][s] + h[3][s];
-        if (c) atomicAdd(reinterpret_cast<unsigned long long *>(at<uint64_t>(a.ws, a.w.counts) + s),
-                         (unsigned long long)c);
+        uint64_t sum = 0;
+        // rotated start: the lanes of a wave read different banks
+        for (uint32_t j = 0; j < kHistCopies; ++j) sum += h[s * kHistCopies + ((j + s) & (kHistCopies - 1u))];
+        if (sum) atomicAdd(reinterpret_cast<unsigned long long *>(at<uint64_t>(a.ws, a.w.counts) + s),
+                           (unsigned long long)sum);
     }
 }
 
 // Super-weight list (ascending, in range, escape code at each index) and
 // finite scales; the scales are copied into the container on the way.
+// Runs first: workgroup 0 also clears the workspace counters.
 __global__ void k_enc_check(EncArgs a) {
     const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
     const uint64_t tid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (tid < 256) at<uint64_t>(a.ws, a.w.counts)[tid] = 0;
+    if (tid < 2) at<uint64_t>(a.ws, a.w.misc)[tid] = 0;
     float *osc = at<float>(a.out, a.sec.scales);
     for (uint64_t r = tid; r < a.rows; r += stride) {
         const float v = a.scales[r];
@@ -150,16 +181,16 @@ __global__ void k_enc_check(EncArgs a) {
 //   f_s = max(1, floor(c_s * 4096 / N)) for present bytes; a shortfall goes
 //   +1 to the present bytes ranked first by (remainder c_s * 4096 mod N
 //   descending, byte ascending); an excess is taken -1 at a time from the
-//   largest f_s > 1 (smallest byte among equals).
+//   largest f_s > 1 (smallest byte among equals), computed here in closed
+//   form.
 __global__ void __launch_bounds__(256) k_enc_quant(EncArgs a) {
-    __shared__ uint64_t rem[256];
+    __shared__ uint64_t key[256];
     __shared__ int32_t f[256];
-    __shared__ int32_t red_v[256];
-    __shared__ int32_t red_s[256];
     __shared__ int32_t total;
     const uint32_t s = threadIdx.x;
-    const uint64_t *counts = at<uint64_t>(a.ws, a.w.counts);
-    const uint64_t c = counts[s];
+    __shared__ uint64_t counts[256];  // read by every thread below: staged in LDS
+    const uint64_t c = at<uint64_t>(a.ws, a.w.counts)[s];
+    counts[s] = c;
     const uint64_t scaled = c * (uint64_t)kProbScale;
     const bool present = c != 0;
     int32_t fs = 0;
@@ -168,7 +199,10 @@ __global__ void __launch_bounds__(256) k_enc_quant(EncArgs a) {
         fs = q > 1 ? (int32_t)q : 1;
     }
     f[s] = fs;
-    rem[s] = present ? scaled % a.n : 0;
+    // key = remainder above the byte's complement, so a larger key ranks
+    // first; an absent byte's key is 0 and never counts (a strictly larger
+    // key is needed)
+    key[s] = present ? ((scaled % a.n) << 8 | (255u - s)) : 0;
     if (s == 0) total = 0;
     __syncthreads();
     atomicAdd(&total, fs);
@@ -176,42 +210,68 @@ __global__ void __launch_bounds__(256) k_enc_quant(EncArgs a) {
     const int32_t deficit = (int32_t)kProbScale - total;
     if (deficit > 0) {
         if (present) {
+            // rank among present bytes by (remainder descending, byte
+            // ascending): one branch-free u64 key compare per byte
             uint32_t rank = 0;
-            for (uint32_t t = 0; t < 256; ++t)
-                if (counts[t] && (rem[t] > rem[s] || (rem[t] == rem[s] && t < s))) ++rank;
+            const uint64_t ks = key[s];
+#pragma unroll 16
+            for (uint32_t t = 0; t < 256; ++t) rank += key[t] > ks ? 1u : 0u;
             if ((int32_t)rank < deficit) f[s] = fs + 1;
         }
         __syncthreads();
-    } else {
-        for (int32_t d = deficit; d < 0; ++d) {
-            // argmax of f over f > 1, smallest byte among equals
-            red_v[s] = f[s] > 1 ? f[s] : -1;
-            red_s[s] = (int32_t)s;
+    } else if (deficit < 0) {
+        // Taking 1 from the largest f > 1 (smallest byte first) E times
+        // lowers the top level evenly: with cost(v) = sum of max(0, f - v)
+        // and v the smallest level with cost(v) < E, every f above v comes
+        // down to v and the remaining E - cost(v) decrements go to the
+        // bytes then at v in ascending order (each leaves the top level
+        // after its one decrement). v = 1 would mean too few f > 1.
+        const int32_t E = -deficit;
+        __shared__ int32_t acc;
+        auto cost = [&](int32_t v) {  // every thread calls it
             __syncthreads();
-            for (uint32_t o = 128; o > 0; o >>= 1) {
-                if (s < o) {
-                    const int32_t v2 = red_v[s + o], s2 = red_s[s + o];
-                    if (v2 > red_v[s] || (v2 == red_v[s] && s2 < red_s[s])) {
-                        red_v[s] = v2;
-                        red_s[s] = s2;
-                    }
-                }
-                __syncthreads();
-            }
-            if (s == 0 && red_v[0] > 0) f[red_s[0]] -= 1;
-            if (s == 0 && red_v[0] <= 0) flag(a.status, EQ_DEV_BAD_INPUT);
+            if (s == 0) acc = 0;
             __syncthreads();
+            if (fs > v) atomicAdd(&acc, fs - v);
+            __syncthreads();
+            return acc;
+        };
+        int32_t lo = 1, hi = (int32_t)kProbScale;  // cost(hi) = 0 < E
+        while (lo < hi) {
+            const int32_t mid = (lo + hi) / 2;
+            if (cost(mid) < E) hi = mid;
+            else lo = mid + 1;
         }
+        const int32_t v = lo;
+        if (v == 1) {
+            if (s == 0) flag(a.status, EQ_DEV_BAD_INPUT);
+        } else {
+            const int32_t r = E - cost(v);
+            uint32_t rank = 0;  // bytes below s at the top level after the cut
+#pragma unroll 16
+            for (uint32_t t = 0; t < 256; ++t) rank += (t < s && f[t] >= v) ? 1u : 0u;
+            __syncthreads();
+            if (fs >= v) f[s] = v - ((int32_t)rank < r ? 1 : 0);
+        }
+        __syncthreads();
     }
-    // cumulative frequencies (serial over 256 entries, thread 0)
-    __shared__ uint32_t cum[257];
-    if (s == 0) {
-        uint32_t acc = 0;
-        for (int t = 0; t < 256; ++t) {
-            cum[t] = acc;
-            acc += (uint32_t)f[t];
+    // cumulative frequencies: exclusive prefix sum over bytes (log-step scan)
+    __shared__ uint32_t cum[256];
+    {
+        uint32_t v = (uint32_t)f[s];
+        cum[s] = v;
+        for (uint32_t o = 1; o < 256; o <<= 1) {
+            __syncthreads();
+            const uint32_t add = s >= o ? cum[s - o] : 0u;
+            __syncthreads();
+            v += add;
+            cum[s] = v;
         }
-        cum[256] = acc;
+        __syncthreads();
+        cum[s] = v - (uint32_t)f[s];
+        __syncthreads();
+    }
+    if (s == 0) {
         // E4M3 NaN codes are only allowed as the escape code; the escape count
         // must match the list
         if (a.dtype == EQ_DTYPE_E4M3) {
@@ -221,7 +281,14 @@ __global__ void __launch_bounds__(256) k_enc_quant(EncArgs a) {
         if (a.esc_enabled ? counts[a.esc_code] != a.n_esc : a.n_esc != 0) flag(a.status, EQ_DEV_BAD_INPUT);
     }
     __syncthreads();
-    at<uint32_t>(a.ws, a.w.table)[s] = (uint32_t)f[s] | (cum[s] << 16);
+    EncSym es;
+    es.rcp = f[s] ? 1.0 / (double)f[s] : 0.0;
+    // 16 f (the emit threshold on x >> 16; f = 4096, a one-symbol table that
+    // never emits, gets 0xFFFF, above any x >> 16 its state reaches)
+    es.fg = (f[s] < (int32_t)kProbScale ? (uint32_t)f[s] << 4 : 0xFFFFu) |
+            ((kProbScale - (uint32_t)f[s]) << 16);
+    es.cum = cum[s];
+    at<EncSym>(a.ws, a.w.table)[s] = es;
     reinterpret_cast<uint16_t *>(a.out + a.sec.freq)[s] = (uint16_t)f[s];
     // header: every byte written; n_words-dependent fields are filled by k_enc_scan
     if (s < kHeaderBytes / 4) reinterpret_cast<uint32_t *>(a.out)[s] = 0;
@@ -251,49 +318,159 @@ __global__ void __launch_bounds__(256) k_enc_quant(EncArgs a) {
     }
 }
 
+// floor(x / f) for 1 <= f <= 4096 and x < f * 2^20 (the state after the
+// encoder's renormalisation), from r = 1/f rounded to binary64 (relative
+// error <= 2^-53): x/f < 2^20, so x*r is within 2^-33 of x/f and the fused
+// multiply-add's one rounding adds at most 2^-33 more; fma(x, r, 2^-14) lies
+// in (x/f, x/f + 2^-13). The fractional part of x/f is 0 or in
+// [1/f, 1 - 1/f] with 1/f >= 2^-12, so truncation gives the exact quotient.
+__device__ __forceinline__ uint32_t enc_div(uint32_t x, double rcp) {
+    return (uint32_t)__builtin_fma((double)x, rcp, 0x1p-14);
+}
+
+// A lane's K symbols of one group, packed four to a word (byte i of the run
+// in bits 8*(i%4) of word i/4); positions past the chunk read as 0.
+template <int K>
+__device__ __forceinline__ void load_run(const uint8_t *sym, uint32_t q0, uint32_t nk,
+                                         uint32_t (&w)[(K + 3) / 4]) {
+    if (K >= 4 && q0 + (uint32_t)K <= nk) {
+        // a full run: one aligned load (q0 and the chunk start are multiples of K)
+        if constexpr (K == 16) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(sym + q0);
+            w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+        } else if constexpr (K == 8) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(sym + q0);
+            w[0] = v.x; w[1] = v.y;
+        } else if constexpr (K == 4) {
+            w[0] = *reinterpret_cast<const uint32_t *>(sym + q0);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < (K + 3) / 4; ++j) w[j] = 0;
+#pragma unroll
+        for (int i = 0; i < K; ++i)
+            if (q0 + (uint32_t)i < nk) w[i / 4] |= (uint32_t)sym[q0 + i] << (8 * (i % 4));
+    }
+}
+
 // One wave per chunk: the rANS encoder of the container's coder, steps
-// walked backwards.
+// walked backwards. Chunk-local word positions p land in ring[p mod 2048];
+// [wpos, nk) holds the chunk's words so far, [flushed, ...) is already in the
+// scratch. Whole 8-word blocks above wpos leave 512 words at a time; at the
+// end every block that holds a word leaves (the part of a block below wpos,
+// or above nk in the tail chunk, is scratch nobody reads).
 template <int K>
 __global__ void __launch_bounds__(kEncThreads) k_enc_chunks(EncArgs a) {
-    __shared__ uint32_t tab[256];
-    for (uint32_t i = threadIdx.x; i < 256; i += blockDim.x) tab[i] = at<uint32_t>(a.ws, a.w.table)[i];
+    __shared__ __align__(16) EncSym tab[256];
+    __shared__ __align__(16) uint16_t rings[kEncWaves][kEncRing];
+    for (uint32_t i = threadIdx.x; i < 256; i += blockDim.x) tab[i] = at<EncSym>(a.ws, a.w.table)[i];
     __syncthreads();
     const uint32_t lane = threadIdx.x & 63u;
-    const uint64_t k = (uint64_t)blockIdx.x * kEncWaves + (threadIdx.x >> 6);
+    const uint32_t wave = threadIdx.x >> 6;
+    const uint64_t k = (uint64_t)blockIdx.x * kEncWaves + wave;
     if (k >= a.n_chunks) return;
+    uint16_t *ring = rings[wave];
     const uint64_t p0 = k * a.Z;
     const uint32_t nk = (uint32_t)(a.n - p0 < a.Z ? a.n - p0 : a.Z);
     const uint8_t *sym = a.sym + p0;
     uint16_t *scr = at<uint16_t>(a.ws, a.w.scratch) + p0;
     constexpr uint32_t G = 64u * K;
+    constexpr int W = (K + 3) / 4;             // packed words per run
+    constexpr int D = K >= 4 ? 64 / K : 16;    // groups per batch (64 bytes per lane for K >= 4)
     const uint32_t groups = (nk + G - 1) / G;
     uint32_t x = kStateLow;
-    uint32_t wpos = nk;  // words fill scr[wpos, nk)
-    for (uint32_t g = groups; g-- > 0;) {
+    uint32_t wpos = nk;                   // words fill [wpos, nk)
+    uint32_t flushed = (uint32_t)round_up(nk, 8);
+
+    // groups ghi-1, ghi-2, ... (D of them, those >= 0) into nxt[0], nxt[1], ...
+    uint32_t nxt[D][W];
+    auto load_batch = [&](uint32_t ghi) {
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+            if (ghi > (uint32_t)d) load_run<K>(sym, (ghi - 1u - (uint32_t)d) * G + lane * K, nk, nxt[d]);
+    };
+    typedef __attribute__((address_space(3))) uint16_t lds_u16;
+    const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_u16 *)ring;  // LDS byte address
+    auto group = [&](uint32_t g, const uint32_t (&w)[W], bool full) {
         const uint32_t q0 = g * G + lane * K;
-        uint8_t run[K];
+        wpos = __builtin_amdgcn_readfirstlane(wpos);  // wave-uniform: keep it scalar
+        // the run's table entries do not depend on the state: all K reads
+        // are issued before the serial steps. In a group that reaches past
+        // the chunk, such a position gets an entry that never emits (16 f
+        // field 0xFFFF) and leaves the state as it is (4096 - f and cum
+        // fields 0), so the steps need no lane mask.
+        EncSym es[K];
 #pragma unroll
-        for (int i = 0; i < K; ++i) run[i] = q0 + (uint32_t)i < nk ? sym[q0 + i] : 0;
-#pragma unroll
-        for (int i = K - 1; i >= 0; --i) {
-            const bool active = q0 + (uint32_t)i < nk;
-            const uint32_t e = tab[run[i]];
-            const uint32_t fr = e & 0xFFFFu, cu = e >> 16;
-            const bool emit = active && (uint64_t)x >= ((uint64_t)fr << 20);
-            const uint64_t m = __builtin_amdgcn_ballot_w64(emit);
-            const uint32_t cnt = (uint32_t)__builtin_popcountll(m);
-            const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-            if (emit) {
-                scr[wpos - cnt + rank] = (uint16_t)(x & 0xFFFFu);
-                x >>= 16;
-            }
-            wpos -= cnt;
-            if (active) {
-                const uint32_t qq = x / fr;
-                x = (qq << kProbBits) + (x - qq * fr) + cu;
+        for (int i = 0; i < K; ++i) {
+            es[i] = tab[(w[i / 4] >> (8 * (i % 4))) & 0xFFu];
+            if (!full && q0 + (uint32_t)i >= nk) {
+                es[i].fg = 0xFFFFu;  // 16 f field above any reachable x >> 16
+                es[i].cum = 0;
             }
         }
+#pragma unroll
+        for (int i = K - 1; i >= 0; --i) {
+            const EncSym e = es[i];
+            // x >= f * 2^20  <=>  x >> 16 >= 16 f  (one compare on the high half)
+            const bool emit = (x >> 16) >= (e.fg & 0xFFFFu);
+            const uint64_t m = __builtin_amdgcn_ballot_w64(emit);
+            const uint32_t cnt = (uint32_t)__builtin_popcountll(m);
+            wpos -= cnt;
+            // slot of this lane's word: wpos + rank (ascending lanes)
+            const uint32_t slot = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)m, wpos));
+            // ring address (slot mod 2048 words), then under an exec mask of
+            // the emitting lanes (set and restored by the scalar unit) the
+            // store of the low 16 bits and x >>= 16
+            uint64_t saved;
+            uint32_t addr;
+            asm volatile("v_and_b32 %1, 0x7ff, %3\n\t"
+                         "v_lshl_add_u32 %1, %1, 1, %4\n\t"
+                         "s_and_saveexec_b64 %0, %5\n\t"
+                         "ds_write_b16 %1, %2\n\t"
+                         "v_lshrrev_b32 %2, 16, %2\n\t"
+                         "s_mov_b64 exec, %0"
+                         : "=&s"(saved), "=&v"(addr), "+v"(x)
+                         : "v"(slot), "s"(ring_lds), "s"(m)
+                         : "memory", "scc");
+            // (x / f) * 4096 + x mod f + cum = x + (x / f) * (4096 - f) + cum
+            const uint32_t qq = enc_div(x, e.rcp);
+            x = x + __umul24(qq, e.fg >> 16) + e.cum;
+        }
+        while (flushed >= wpos + kEncFlush) {
+            const uint32_t b = flushed - kEncFlush + lane * 8u;
+            *reinterpret_cast<uint4 *>(scr + b) =
+                *reinterpret_cast<const uint4 *>(ring + (b & (kEncRing - 1u)));
+            flushed -= kEncFlush;
+        }
+    };
+
+    // double-buffered batches: the next D groups' symbols are in flight while
+    // the current D groups are encoded
+    load_batch(groups);
+    for (uint32_t ghi = groups; ghi > 0;) {
+        uint32_t cur[D][W];
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+#pragma unroll
+            for (int j = 0; j < W; ++j) cur[d][j] = nxt[d][j];
+        const uint32_t glo = ghi > (uint32_t)D ? ghi - (uint32_t)D : 0u;
+        if (glo) load_batch(glo);
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            if (ghi > (uint32_t)d) {
+                const uint32_t g = ghi - 1u - (uint32_t)d;
+                if ((g + 1u) * G <= nk) group(g, cur[d], true);
+                else group(g, cur[d], false);
+            }
+        }
+        ghi = glo;
+    }
+    {
+        const uint32_t lo = wpos & ~7u;
+        const uint32_t b = lo + lane * 8u;
+        if (b < flushed)
+            *reinterpret_cast<uint4 *>(scr + b) = *reinterpret_cast<const uint4 *>(ring + (b & (kEncRing - 1u)));
     }
     at<uint32_t>(a.out, a.sec.states)[k * kLanes + lane] = x;
     if (lane == 0) at<uint32_t>(a.ws, a.w.wstart)[k] = wpos;
@@ -353,8 +530,36 @@ __global__ void __launch_bounds__(1024) k_enc_scan(EncArgs a) {
     }
 }
 
-// Words to their final place (one wave per chunk; zero padding words), then
-// the escape list and the zero gaps between sections (workgroup 0).
+// Eight words starting S words into the 16 words held by lo and hi.
+template <uint32_t S>
+__device__ __forceinline__ uint4 words_at(uint4 lo, uint4 hi) {
+    const uint32_t d[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    constexpr uint32_t h = S / 2;
+    uint32_t o[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        o[t] = (S & 1u) ? __builtin_amdgcn_alignbyte(d[h + t + 1], d[h + t], 2) : d[h + t];
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+__device__ __forceinline__ uint4 words_at(uint32_t s, uint4 lo, uint4 hi) {
+    switch (s) {  // wave-uniform
+        case 0: return words_at<0>(lo, hi);
+        case 1: return words_at<1>(lo, hi);
+        case 2: return words_at<2>(lo, hi);
+        case 3: return words_at<3>(lo, hi);
+        case 4: return words_at<4>(lo, hi);
+        case 5: return words_at<5>(lo, hi);
+        case 6: return words_at<6>(lo, hi);
+        default: return words_at<7>(lo, hi);
+    }
+}
+
+// Words to their final place (one wave per chunk, 8 words per lane and
+// block; padding words are zero), then the escape list and the zero gaps
+// between sections (workgroup 0). The chunk's words start at scratch
+// position wpos, s = wpos mod 8 words past an aligned block; the read of the
+// block after the last one stays inside the scratch's 16 spare words.
 __global__ void __launch_bounds__(kEncThreads) k_enc_copy(EncArgs a) {
     const uint32_t lane = threadIdx.x & 63u;
     const uint64_t k = (uint64_t)blockIdx.x * kEncWaves + (threadIdx.x >> 6);
@@ -363,10 +568,40 @@ __global__ void __launch_bounds__(kEncThreads) k_enc_copy(EncArgs a) {
         const uint32_t nk = (uint32_t)(a.n - p0 < a.Z ? a.n - p0 : a.Z);
         const uint32_t ws = at<uint32_t>(a.ws, a.w.wstart)[k];
         const uint32_t cnt = nk - ws;
-        const uint32_t padded = (uint32_t)round_up(cnt, kWordPad);
-        const uint16_t *src = at<uint16_t>(a.ws, a.w.scratch) + p0 + ws;
-        uint16_t *dst = at<uint16_t>(a.out, a.sec.words) + at<uint64_t>(a.ws, a.w.first)[k];
-        for (uint32_t i = lane; i < padded; i += 64u) dst[i] = i < cnt ? src[i] : 0;
+        const uint32_t nblk = (uint32_t)round_up(cnt, kWordPad) / 8u;
+        const uint32_t s = ws & 7u;
+        const uint4 *src = reinterpret_cast<const uint4 *>(at<uint16_t>(a.ws, a.w.scratch) + p0 + (ws - s));
+        uint4 *dst = reinterpret_cast<uint4 *>(at<uint16_t>(a.out, a.sec.words) + at<uint64_t>(a.ws, a.w.first)[k]);
+        constexpr uint32_t U = 4;  // blocks per lane in flight
+        for (uint32_t j0 = 0; j0 < nblk; j0 += 64u * U) {
+            uint4 lo[U], hi[U];
+#pragma unroll
+            for (uint32_t u = 0; u < U; ++u) {
+                const uint32_t j = j0 + u * 64u + lane;
+                if (j < nblk) {
+                    lo[u] = src[j];
+                    hi[u] = src[j + 1];
+                }
+            }
+#pragma unroll
+            for (uint32_t u = 0; u < U; ++u) {
+                const uint32_t j = j0 + u * 64u + lane;
+                if (j < nblk) {
+                    uint4 v = words_at(s, lo[u], hi[u]);
+                    const uint32_t left = cnt - 8u * j;  // words of the chunk in this block
+                    if (left < 8u) {
+                        uint32_t o[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                        for (uint32_t t = 0; t < 4; ++t) {
+                            if (2u * t >= left) o[t] = 0;
+                            else if (2u * t + 1u == left) o[t] &= 0xFFFFu;
+                        }
+                        v = make_uint4(o[0], o[1], o[2], o[3]);
+                    }
+                    dst[j] = v;
+                }
+            }
+        }
     }
     if (blockIdx.x != 0) return;
     const uint64_t *misc = at<uint64_t>(a.ws, a.w.misc);
@@ -457,10 +692,11 @@ eq_status eq_encode_device(const eq_tensor_desc *d, const uint8_t *d_symbols, co
     hipStream_t s = static_cast<hipStream_t>(stream);
     const uint32_t cgrid = (uint32_t)((n_chunks + kEncWaves - 1) / kEncWaves);
     if (n_chunks > 0xFFFFFFFFull / 4) return EQ_EINVAL;
-    hipLaunchKernelGGL(k_enc_zero, dim3(1), dim3(256), 0, s, a);
-    const uint64_t hgrid = (n / 16 + 255) / 256;
-    hipLaunchKernelGGL(k_enc_hist, dim3((uint32_t)(hgrid < 2048 ? (hgrid ? hgrid : 1) : 2048)), dim3(256), 0, s, a);
     hipLaunchKernelGGL(k_enc_check, dim3(64), dim3(256), 0, s, a);
+    // about 32 KiB of symbols per workgroup and pass, at most kHistMaxGrid workgroups
+    const uint64_t hg = (n + 32767) / 32768;
+    const uint32_t hgrid = (uint32_t)(hg < kHistMaxGrid ? (hg ? hg : 1) : kHistMaxGrid);
+    hipLaunchKernelGGL(k_enc_hist, dim3(hgrid), dim3(256), 0, s, a);
     hipLaunchKernelGGL(k_enc_quant, dim3(1), dim3(256), 0, s, a);
     switch (K) {
         case 1: launch_chunks<1>(cgrid, s, a); break;

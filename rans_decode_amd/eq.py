@@ -345,10 +345,11 @@ EQ_DEV_BAD_INPUT = 4
 
 def eq_encode_device(dtype: int, rows: int, cols: int, d_symbols, d_scales, d_esc_idx=None,
                      d_esc_val=None, esc_code: int = 0, chunk_symbols: int = 65536, lane_run: int = 8,
-                     workspace=None, out=None, stream=None):
+                     workspace=None, out=None, stream=None, d_len=None, d_status=None):
     """Device-side encode (torch tensors on the GPU). Returns (out, d_len,
     d_status) without synchronising: out[:int(d_len)] is the container once
-    the stream has run."""
+    the stream has run. A d_status passed in is not cleared (flags of
+    several calls accumulate)."""
     torch = _torch()
     n_esc = 0 if d_esc_idx is None else int(d_esc_idx.numel())
     d = eq_tensor_desc(dtype=dtype, lane_run=lane_run, rows=rows, cols=cols,
@@ -361,8 +362,10 @@ def eq_encode_device(dtype: int, rows: int, cols: int, d_symbols, d_scales, d_es
         workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
     if out is None:
         out = torch.empty(max(cap, 16), dtype=torch.uint8, device=dev)
-    d_len = torch.zeros(1, dtype=torch.int64, device=dev)
-    d_status = torch.zeros(1, dtype=torch.int32, device=dev)
+    if d_len is None:
+        d_len = torch.zeros(1, dtype=torch.int64, device=dev)
+    if d_status is None:
+        d_status = torch.zeros(1, dtype=torch.int32, device=dev)
     _check("eq_encode_device", _lib.eq_encode_device(
         ctypes.byref(d), d_symbols.data_ptr(), d_scales.data_ptr(),
         d_esc_idx.data_ptr() if n_esc else None, d_esc_val.data_ptr() if n_esc else None, n_esc,

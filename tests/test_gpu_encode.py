@@ -78,9 +78,11 @@ def test_random_layouts():
         Z = 64 * K * int(rng.integers(1, 9))
         n = int(rng.integers(1, 5 * Z))
         n = max(16, n - n % 16) if it % 2 else n
-        k = int(rng.integers(1, 60))
+        # every tenth layout: all 256 codes near-uniform (~8 bits per symbol,
+        # the most words a chunk can hold in flight)
+        k = 256 if it % 10 == 9 else int(rng.integers(1, 60))
         present = rng.choice(256, size=k, replace=False)
-        w = rng.exponential(1.0, k) ** 3 + 1e-6
+        w = rng.uniform(0.5, 1.0, k) if k == 256 else rng.exponential(1.0, k) ** 3 + 1e-6
         sym = present[rng.choice(k, size=n, p=w / w.sum())].astype(np.uint8)
         divs = [d for d in range(1, min(n, 64) + 1) if n % d == 0]
         rows = int(rng.choice(divs))
