@@ -46,6 +46,12 @@ namespace {
 #ifndef EQ_RENORM_BRANCHLESS
 #define EQ_RENORM_BRANCHLESS 1
 #endif
+#ifndef EQ_SADDR_STORE
+#define EQ_SADDR_STORE 1  // K = 8 bf16 stores with a scalar base address
+#endif
+#ifndef EQ_LUT_SCAN
+#define EQ_LUT_SCAN 1   // slot table by a running maximum of start marks (else a binary search per slot)
+#endif
 #ifndef EQ_LUT8
 #define EQ_LUT8 1
 #endif
@@ -54,6 +60,11 @@ namespace {
 #endif
 #ifndef EQ_NT_STORES
 #define EQ_NT_STORES 1
+#endif
+#if EQ_NT_STORES
+#define EQ_NT_SUFFIX " nt"
+#else
+#define EQ_NT_SUFFIX ""
 #endif
 constexpr int kWaves = EQ_WAVES;
 constexpr int kThreads = 64 * kWaves;
@@ -194,8 +205,21 @@ __device__ __forceinline__ void raise_flag(uint32_t *status, uint32_t bits, uint
 // Slot table of the tensor: for every slot in [0, 4096) the byte s with
 // cum[s] <= slot < cum[s] + f[s], packed as s | f << 8 | (slot - cum[s]) << 20
 // (f <= 4095 here; a one-symbol tensor never builds a table).
-__device__ __forceinline__ void build_lut(const uint16_t *freq, LutEnt *lut, uint32_t *cum) {
+__device__ __forceinline__ void build_lut(const uint16_t *freq, LutEnt *lut, uint32_t *scr) {
     const uint32_t tid = threadIdx.x;
+    uint32_t *cum = scr;  // [257]
+#if EQ_LUT_SCAN
+    // Every present byte s marks its first slot cum[s] with s + 1; the byte
+    // of a slot is then the running maximum of the marks up to it (present
+    // bytes have increasing cum). Each thread owns P consecutive slots.
+    constexpr uint32_t P = 4096u / kThreads;
+    static_assert(P * kThreads == 4096u, "slots per thread");
+    uint32_t *wmax = scr + 260;                                     // [kWaves]
+    uint16_t *mark = reinterpret_cast<uint16_t *>(scr + 272);       // [4096]
+#pragma unroll
+    for (uint32_t j = 0; j < P; ++j) mark[P * tid + j] = 0;
+    __syncthreads();
+#endif
     if (tid < 64) {
         uint32_t f[4];
         uint32_t s = 0;
@@ -214,11 +238,44 @@ __device__ __forceinline__ void build_lut(const uint16_t *freq, LutEnt *lut, uin
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             cum[4 * tid + i] = c;
+#if EQ_LUT_SCAN
+            if (f[i] && c < 4096u) mark[c] = (uint16_t)(4 * tid + i + 1);
+#endif
             c += f[i];
         }
         if (tid == 63) cum[256] = incl;
     }
     __syncthreads();
+#if EQ_LUT_SCAN
+    uint32_t run[P];
+    uint32_t m = 0;
+#pragma unroll
+    for (uint32_t j = 0; j < P; ++j) {
+        const uint32_t v = mark[P * tid + j];
+        m = v > m ? v : m;
+        run[j] = m;
+    }
+    // exclusive running maximum over the threads before this one
+    const uint32_t lane = tid & 63u, wave = tid >> 6;
+    uint32_t incl = m;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t v = __shfl_up(incl, o, 64);
+        if (lane >= (uint32_t)o) incl = v > incl ? v : incl;
+    }
+    uint32_t before = __shfl_up(incl, 1, 64);
+    if (lane == 0) before = 0;
+    if (lane == 63) wmax[wave] = incl;
+    __syncthreads();
+    for (uint32_t w = 0; w < wave; ++w) before = wmax[w] > before ? wmax[w] : before;
+#pragma unroll
+    for (uint32_t j = 0; j < P; ++j) {
+        const uint32_t slot = P * tid + j;
+        const uint32_t sym = (run[j] > before ? run[j] : before) - 1u;
+        const uint32_t c0 = cum[sym];
+        lut[slot] = make_ent(sym, cum[sym + 1] - c0, slot - c0);
+    }
+#else
     for (uint32_t slot = tid; slot < 4096u; slot += kThreads) {
         uint32_t lo = 0, hi = 256;  // cum[lo] <= slot < cum[hi]
 #pragma unroll
@@ -229,6 +286,7 @@ __device__ __forceinline__ void build_lut(const uint16_t *freq, LutEnt *lut, uin
         const uint32_t f = cum[lo + 1] - cum[lo];
         lut[slot] = make_ent(lo, f, slot - cum[lo]);
     }
+#endif
     __syncthreads();
 }
 
@@ -526,7 +584,30 @@ struct Chunk {
                     }
                     if (esc_loc < g0 + G) patch_packed(g0, pk);
                     uint16_t *gb = ob + g0;  // wave-uniform base of the group
-                    store_packed(reinterpret_cast<char *>(gb) + lane * (2u * K), pk);
+#if EQ_SADDR_STORE
+                    if constexpr (K == 8) {
+                        // scalar base + the lane's constant 32-bit offset: no
+                        // per-group 64-bit address arithmetic on the VALU.
+                        // Wait states the compiler cannot see inside the asm:
+                        // 5 before (a VALU write of the base SGPRs, e.g. by
+                        // v_readfirstlane, before a memory instruction reads
+                        // them) and 1 after (a wide store's data registers are
+                        // not rewritten by the next VALU instruction)
+                        const uint64_t b = reinterpret_cast<uint64_t>(gb);
+                        // (readfirstlane returns int: widen through uint32_t,
+                        // never by sign extension)
+                        const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+                        const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+                        const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
+                        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+                        const u32x4 v = {pk[0], pk[1], pk[2], pk[3]};
+                        asm volatile("s_nop 4\n\tglobal_store_dwordx4 %0, %1, %2" EQ_NT_SUFFIX "\n\ts_nop 0"
+                                     :
+                                     : "v"(lane * 16u), "v"(v), "s"(sb)
+                                     : "memory");
+                    } else
+#endif
+                    store_packed(reinterpret_cast<uint64_t>(gb) + lane * (2u * K), pk);
                     advance_row();
                     return;
                 }
@@ -648,23 +729,29 @@ struct Chunk {
         } while (esc_loc < g0 + G);
     }
 
-    __device__ __forceinline__ void store_packed(char *dst, const uint32_t *pk) {
+    // dst is a global-memory address (the output buffer)
+    __device__ __forceinline__ void store_packed(uint64_t dst, const uint32_t *pk) {
+        typedef __attribute__((address_space(1))) uint16_t g16;
+        typedef __attribute__((address_space(1))) uint32_t g32;
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        typedef __attribute__((address_space(1))) u32x2 g64;
         if constexpr (K == 1) {
-            *reinterpret_cast<uint16_t *>(dst) = (uint16_t)pk[0];
+            *reinterpret_cast<g16 *>(dst) = (uint16_t)pk[0];
         } else if constexpr (K == 2) {
-            *reinterpret_cast<uint32_t *>(dst) = pk[0];
+            *reinterpret_cast<g32 *>(dst) = pk[0];
         } else if constexpr (K == 4) {
-            *reinterpret_cast<uint2 *>(dst) = make_uint2(pk[0], pk[1]);
+            const u32x2 v = {pk[0], pk[1]};
+            *reinterpret_cast<g64 *>(dst) = v;
         } else {
+            typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+            typedef __attribute__((address_space(1))) u32x4 g128;
 #pragma unroll
             for (int i = 0; i < K / 8; ++i) {
-#if EQ_NT_STORES
-                typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
                 u32x4 v = {pk[4 * i], pk[4 * i + 1], pk[4 * i + 2], pk[4 * i + 3]};
-                __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(dst) + i);
+#if EQ_NT_STORES
+                __builtin_nontemporal_store(v, reinterpret_cast<g128 *>(dst) + i);
 #else
-                reinterpret_cast<uint4 *>(dst)[i] =
-                    make_uint4(pk[4 * i], pk[4 * i + 1], pk[4 * i + 2], pk[4 * i + 3]);
+                reinterpret_cast<g128 *>(dst)[i] = v;
 #endif
             }
         }
@@ -862,6 +949,8 @@ __global__ void __launch_bounds__(kThreads) k_decode(LArgs a) {
     constexpr bool GEMV = OUT == OUT_GEMV;
     __shared__ LutEnt lut[4096];
     __shared__ __attribute__((aligned(16))) uint16_t rings[kWaves][kRingAlloc];
+    // the slot-table build's scratch (cum, wave maxima, 4096 u16 marks) lives in the rings
+    static_assert(!EQ_LUT_SCAN || sizeof(rings) >= 272 * 4 + 4096 * 2, "rings too small for the table build");
 
     const uint32_t wg = blockIdx.x;
     uint32_t ti = 0;
