@@ -470,6 +470,7 @@ def bench_encode(args):
     import synth
     from rans_decode_amd import eq
 
+    codec = CODECS[args.codec]
     specs = synth.config_specs(4)
     tensors = []
     t0 = time.perf_counter()
@@ -497,7 +498,7 @@ def bench_encode(args):
             sp = d["spec"]
             eq.eq_encode_device(sp.dtype, sp.rows, sp.cols, d["sym"], d["sc"], d["ei"], d["ev"],
                                 d["code"], synth.CHUNK_SYMBOLS, args.lane_run, workspace=ws,
-                                out=o, stream=stream, d_len=ln, d_status=st)
+                                out=o, stream=stream, d_len=ln, d_status=st, codec=codec)
 
     for _ in range(args.warmup):
         block()
@@ -505,7 +506,7 @@ def bench_encode(args):
     if any(int(st.item()) for st in stats):
         raise RuntimeError("device encode flagged its input")
     # byte-for-byte against the host encoder (its containers, built or cached)
-    _, host = build_block(4, 0, args.lane_run)
+    _, host = build_block(4, 0, args.lane_run, codec=codec)
     for i, (c, o, ln) in enumerate(zip(host, outs, lens)):
         got = o[:int(ln.item())].cpu().numpy()
         if got.size != c.host.size or not np.array_equal(got, c.host):
@@ -533,7 +534,7 @@ def bench_encode(args):
         tab = eq.build_tables(t.symbols)
         eq.encode_host(tab, sp.dtype, sp.rows, sp.cols, t.symbols, t.scales, t.esc_idx if esc else None,
                        t.esc_val if esc else None, esc_code=t.esc_code if esc else 0,
-                       chunk_symbols=synth.CHUNK_SYMBOLS, lane_run=args.lane_run)
+                       chunk_symbols=synth.CHUNK_SYMBOLS, lane_run=args.lane_run, codec=codec)
         host_enc_s += time.perf_counter() - t_enc0
         del t
     n = sum(sp.n for sp in specs)
@@ -543,12 +544,14 @@ def bench_encode(args):
     cont_bytes = sum(int(ln.item()) for ln in lens)
     algo = 2 * n + cont_bytes
     rec = {
-        "metric": "device-side encode of the 70B-shaped block (histogram, quantiser, rANS encode, container)",
+        "metric": "device-side encode of the 70B-shaped block (histogram, quantiser, rANS encode, container)"
+                  if codec == 0 else
+                  "device-side encode of the 70B-shaped block (histogram, Huffman code, encode, container)",
         "value": round(n / (f * 1e-3) / 1e9, 2), "unit": "G symbols/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(f, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "u32", "data": "synthetic",
         "config": {"workload": "70B-shaped block, 855,638,016 int8 codes (2.1-bit Laplace), 4 super weights, "
-                               f"64 Ki chunks, K={args.lane_run}; one eq_encode_device call per tensor",
+                               f"64 Ki chunks, K={args.lane_run}; {args.codec} codec; one eq_encode_device call per tensor",
                    "weights": n},
         "kernel_ms": {"mean": round(f, 4), "median": round(float(np.median(ms)), 4),
                       "min": round(float(np.min(ms)), 4)},
@@ -604,9 +607,34 @@ def bench_drift(args):
         if not np.array_equal(sym.cpu().numpy(), t.symbols):
             raise RuntimeError("decoded symbols differ from the encoded ones")
         f = float(np.mean(ms))
+        # the same container from the device encoder: byte-identical, and its time
+        dsym = torch.from_numpy(t.symbols).cuda()
+        dsc = torch.from_numpy(t.scales).cuda()
+        ws = torch.empty(int(eq._lib.eq_encode_device_workspace(t.spec.rows, t.spec.cols, synth.CHUNK_SYMBOLS)),
+                         dtype=torch.uint8, device="cuda")
+        dout = torch.empty(int(eq._lib.eq_encode_device_bound(t.spec.rows, t.spec.cols, synth.CHUNK_SYMBOLS, 0)),
+                           dtype=torch.uint8, device="cuda")
+        enc = lambda: eq.eq_encode_device(t.spec.dtype, t.spec.rows, t.spec.cols, dsym, dsc,  # noqa: E731
+                                          chunk_symbols=synth.CHUNK_SYMBOLS, lane_run=args.lane_run,
+                                          workspace=ws, out=dout, seg_chunks=seg)
+        _, dlen, dst = enc()
+        torch.cuda.synchronize()
+        if int(dst.item()) or not np.array_equal(dout[:int(dlen.item())].cpu().numpy(), blob):
+            raise RuntimeError("device encoder's container differs from the host encoder's")
+        for _ in range(args.warmup):
+            enc()
+        ems = []
+        for _ in range(args.steps):
+            s0, e0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s0.record()
+            enc()
+            e0.record()
+            torch.cuda.synchronize()
+            ems.append(s0.elapsed_time(e0))
         res[name] = {"container_bytes": int(blob.size), "bits_per_weight": round(8.0 * blob.size / n, 4),
-                     "kernel_ms": round(f, 4), "bf16_GBps": round(2 * n / (f * 1e-3) / 1e9, 1)}
-        del c, out, sym
+                     "kernel_ms": round(f, 4), "bf16_GBps": round(2 * n / (f * 1e-3) / 1e9, 1),
+                     "device_encode_ms": round(float(np.mean(ems)), 4)}
+        del c, out, sym, dsym, dsc, ws, dout
     rec = {
         "metric": "adaptive (per-segment) frequency tables vs one table on a tensor with drifting statistics",
         "value": round(res["one_table"]["container_bytes"] / res["per_8_chunks"]["container_bytes"], 4),

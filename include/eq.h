@@ -260,25 +260,31 @@ eq_status eq_decode_gemv_bf16(const eq_block *b, const uint16_t *const *d_x, flo
                               void *stream);
 
 /*
- * eq_encode_device -- the encoder of eq_encode_host (rANS codec) on the GPU:
- * histogram, the same 12-bit quantiser (as eq_build_tables), chunk-parallel
+ * eq_encode_device -- the encoder of eq_encode_host on the GPU, for every
+ * container variant: rANS with one table, rANS with one table per segment of
+ * seg_chunks chunks, Huffman. Histogram(s), the same 12-bit quantiser (as
+ * eq_build_tables) or the same length-limited Huffman code, chunk-parallel
  * interleaved encoding, container assembly; the container is byte-for-byte
- * what eq_encode_host(eq_build_tables(symbols), d, ...) writes. This is the
- * offline ANS compression of technical component 2 of the EntQuant summary
- * (flatten, ANS-compress, store bitstream + scales + metadata), done where
- * the weights already are.
- * d: as for eq_encode_host (codec EQ_CODEC_RANS with one table per tensor,
- *    else EQ_EUNSUPPORTED). Device pointers: d_symbols (rows*cols bytes, 16-byte
- *    aligned), d_scales (rows fp32), d_esc_idx / d_esc_bf16 (n_esc entries,
- *    may be NULL when n_esc == 0), d_workspace (workspace_bytes >=
- *    eq_encode_device_workspace(), 16-byte aligned, contents ignored), d_out
- *    (cap >= eq_encode_device_bound(), 16-byte aligned), d_out_len (device u64
- *    receiving the container size; may be NULL), d_status (device u32, caller
- *    zeroed, may be NULL: EQ_DEV_BAD_INPUT when a symbol, escape list or
- *    scale is invalid; the container is then unspecified).
+ * what eq_encode_host writes for the same descriptor with the tables built
+ * from the symbols (eq_build_tables; with seg_chunks, tables NULL). This is
+ * the offline ANS compression of technical component 2 of the EntQuant
+ * summary (flatten, ANS-compress, store bitstream + scales + metadata), done
+ * where the weights already are.
+ * d: as for eq_encode_host (codec EQ_CODEC_RANS or EQ_CODEC_HUFFMAN;
+ *    seg_chunks 0 or a multiple of 8 with the rANS codec, else EQ_EINVAL).
+ *    Device pointers: d_symbols (rows*cols bytes, 16-byte aligned), d_scales
+ *    (rows fp32), d_esc_idx / d_esc_bf16 (n_esc entries, may be NULL when
+ *    n_esc == 0), d_workspace (workspace_bytes >= eq_encode_device_workspace(),
+ *    16-byte aligned, contents ignored), d_out (cap >= eq_encode_device_bound(),
+ *    16-byte aligned), d_out_len (device u64 receiving the container size; may
+ *    be NULL), d_status (device u32, caller zeroed, may be NULL:
+ *    EQ_DEV_BAD_INPUT when a symbol, escape list or scale is invalid; the
+ *    container is then unspecified).
+ * eq_encode_device_bound is an upper bound for every codec and segment size
+ * (lane states and the most tables included).
  * Enqueues six kernels on stream; never allocates or synchronises.
- * Errors: EQ_EINVAL (arguments), EQ_ERANGE (workspace or cap too small),
- * EQ_EUNSUPPORTED (codec), EQ_EHIP (launch).
+ * Errors: EQ_EINVAL (arguments, codec, segment size), EQ_ERANGE (workspace or
+ * cap too small), EQ_EHIP (launch).
  */
 uint64_t eq_encode_device_bound(uint64_t rows, uint64_t cols, uint32_t chunk_symbols, uint64_t n_esc);
 uint64_t eq_encode_device_workspace(uint64_t rows, uint64_t cols, uint32_t chunk_symbols);

@@ -59,12 +59,17 @@ constexpr uint32_t kEncRing = 2048;   // words of a wave's output ring
 constexpr uint32_t kHistMaxGrid = 1024;  // histogram workgroups at most (4 per CU)
 constexpr uint32_t kEncFlush = 512;   // words per ring flush (8 per lane)
 
+// Tables a container can have: one, or one per segment of seg_chunks chunks
+// (a multiple of 8), so at most ceil(n_chunks / 8).
+__host__ __device__ inline uint64_t max_tables(uint64_t n_chunks) { return n_chunks > 8 ? (n_chunks + 7) / 8 : 1; }
+
 // Workspace layout (bytes from the start; all 256-byte aligned).
 struct WsLayout {
-    uint64_t counts;   // 256 x u64
-    uint64_t table;    // 256 x EncSym
-    uint64_t misc;     // u64 n_words, u64 total
+    uint64_t counts;   // tables x 256 x u64
+    uint64_t table;    // tables x 256 x EncSym (rANS), or 256 x u32 Huffman codewords
+    uint64_t misc;     // u64 n_words, u64 total, u64 escape codes seen
     uint64_t wstart;   // n_chunks x u32: first word of the chunk inside its scratch region
+    uint64_t wcount;   // n_chunks x u32: the chunk's word count
     uint64_t first;    // n_chunks x u64: first word in the container
     uint64_t scratch;  // n + 16 x u16 (chunk k uses [k*Z, k*Z + nk); the tail chunk's
                        // last aligned block and the copy's read-ahead go past n)
@@ -79,10 +84,12 @@ __host__ __device__ inline WsLayout ws_layout(uint64_t n, uint64_t n_chunks) {
         at = start + bytes;
         return start;
     };
-    w.counts = place(256 * 8);
-    w.table = place(256 * sizeof(EncSym));
-    w.misc = place(16);
+    const uint64_t tabs = max_tables(n_chunks);
+    w.counts = place(tabs * 256 * 8);
+    w.table = place(tabs * 256 * sizeof(EncSym));
+    w.misc = place(24);
     w.wstart = place(n_chunks * 4);
+    w.wcount = place(n_chunks * 4);
     w.first = place(n_chunks * 8);
     w.scratch = place((n + 16) * 2);
     w.total = round_up(at, 256);
@@ -100,6 +107,9 @@ struct EncArgs {
     uint32_t *status;
     uint64_t rows, cols, n, n_chunks, n_esc;
     uint32_t Z, K, dtype, esc_enabled, esc_code;
+    uint32_t codec, seg;  // codec; chunks per table segment (0: one table)
+    uint64_t n_tab;       // tables in the container
+    uint64_t seg_syms;    // symbols per table segment (n with one table)
     WsLayout w;
     Sections sec;  // n_words-independent offsets (freq, scales, dir, states, words)
 };
@@ -124,8 +134,12 @@ __global__ void __launch_bounds__(256) k_enc_hist(EncArgs a) {
     for (uint32_t i = threadIdx.x; i < 256 * kHistCopies; i += blockDim.x) h[i] = 0;
     __syncthreads();
     const uint32_t c = threadIdx.x & (kHistCopies - 1u);
-    const uint64_t n16 = a.n / 16;
-    const uint4 *v = reinterpret_cast<const uint4 *>(a.sym);
+    // this grid row's table segment (a multiple of 512 symbols from the start)
+    const uint64_t base = (uint64_t)blockIdx.y * a.seg_syms;
+    const uint64_t len = a.n - base < a.seg_syms ? a.n - base : a.seg_syms;
+    const uint8_t *sym = a.sym + base;
+    const uint64_t n16 = len / 16;
+    const uint4 *v = reinterpret_cast<const uint4 *>(sym);
     const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
     auto count4 = [&](uint32_t wd) {
 #pragma unroll
@@ -141,16 +155,17 @@ __global__ void __launch_bounds__(256) k_enc_hist(EncArgs a) {
         const uint4 q0 = v[i];
         count4(q0.x); count4(q0.y); count4(q0.z); count4(q0.w);
     }
-    for (uint64_t j = n16 * 16 + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; j < a.n; j += stride)
-        atomicAdd(&h[a.sym[j] * kHistCopies + c], 1u);
+    for (uint64_t j = n16 * 16 + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; j < len; j += stride)
+        atomicAdd(&h[sym[j] * kHistCopies + c], 1u);
     __syncthreads();
     if (threadIdx.x < 256) {
         const uint32_t s = threadIdx.x;
         uint64_t sum = 0;
         // rotated start: the lanes of a wave read different banks
         for (uint32_t j = 0; j < kHistCopies; ++j) sum += h[s * kHistCopies + ((j + s) & (kHistCopies - 1u))];
-        if (sum) atomicAdd(reinterpret_cast<unsigned long long *>(at<uint64_t>(a.ws, a.w.counts) + s),
-                           (unsigned long long)sum);
+        if (sum)
+            atomicAdd(reinterpret_cast<unsigned long long *>(at<uint64_t>(a.ws, a.w.counts) + 256 * blockIdx.y + s),
+                      (unsigned long long)sum);
     }
 }
 
@@ -160,8 +175,8 @@ __global__ void __launch_bounds__(256) k_enc_hist(EncArgs a) {
 __global__ void k_enc_check(EncArgs a) {
     const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
     const uint64_t tid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (tid < 256) at<uint64_t>(a.ws, a.w.counts)[tid] = 0;
-    if (tid < 2) at<uint64_t>(a.ws, a.w.misc)[tid] = 0;
+    for (uint64_t i = tid; i < a.n_tab * 256; i += stride) at<uint64_t>(a.ws, a.w.counts)[i] = 0;
+    if (tid < 3) at<uint64_t>(a.ws, a.w.misc)[tid] = 0;
     float *osc = at<float>(a.out, a.sec.scales);
     for (uint64_t r = tid; r < a.rows; r += stride) {
         const float v = a.scales[r];
@@ -176,8 +191,48 @@ __global__ void k_enc_check(EncArgs a) {
     }
 }
 
-// Quantiser + header + frequency section (one workgroup of 256 threads, one
-// symbol per thread):
+// Container header (one thread; the caller has zeroed its 256 bytes): the
+// fields that do not depend on the word counts (k_enc_scan adds those).
+__device__ __forceinline__ void write_header(const EncArgs &a) {
+    uint8_t *b = a.out;
+    *reinterpret_cast<uint32_t *>(b + H_MAGIC) = kMagic;
+    *reinterpret_cast<uint16_t *>(b + H_VERSION) = kVersion;
+    b[H_DTYPE] = (uint8_t)a.dtype;
+    b[H_FLAGS] = (a.esc_enabled ? kFlagEsc : 0) | (a.seg ? kFlagSeg : 0);
+    *reinterpret_cast<uint64_t *>(b + H_ROWS) = a.rows;
+    *reinterpret_cast<uint64_t *>(b + H_COLS) = a.cols;
+    *reinterpret_cast<uint64_t *>(b + H_N) = a.n;
+    *reinterpret_cast<uint32_t *>(b + H_CHUNK) = a.Z;
+    *reinterpret_cast<uint32_t *>(b + H_LANE_RUN) = a.K;
+    *reinterpret_cast<uint32_t *>(b + H_LANES) = kLanes;
+    *reinterpret_cast<uint32_t *>(b + H_PROB_BITS) = a.codec == kCodecHuffman ? kHuffMaxLen : kProbBits;
+    *reinterpret_cast<uint64_t *>(b + H_NCHUNKS) = a.n_chunks;
+    *reinterpret_cast<uint64_t *>(b + H_NESC) = a.n_esc;
+    b[H_ESC_CODE] = a.esc_enabled ? (uint8_t)a.esc_code : 0;
+    *reinterpret_cast<uint64_t *>(b + H_OFF_FREQ) = a.sec.freq;
+    *reinterpret_cast<uint64_t *>(b + H_OFF_SCALES) = a.sec.scales;
+    *reinterpret_cast<uint64_t *>(b + H_OFF_DIR) = a.sec.dir;
+    *reinterpret_cast<uint64_t *>(b + H_OFF_STATES) = a.sec.states;
+    *reinterpret_cast<uint64_t *>(b + H_OFF_WORDS) = a.sec.words;
+    *reinterpret_cast<uint32_t *>(b + H_CODEC) = a.codec;
+    *reinterpret_cast<uint32_t *>(b + H_SEG) = a.seg;
+}
+
+// Per-table checks (thread 0): E4M3 NaN codes only as the escape code; the
+// escape codes seen are summed for k_enc_scan, which compares the total with
+// the list.
+__device__ __forceinline__ void check_counts(const EncArgs &a, const uint64_t *counts) {
+    if (a.dtype == EQ_DTYPE_E4M3) {
+        if (counts[0x7F] && !(a.esc_enabled && a.esc_code == 0x7Fu)) flag(a.status, EQ_DEV_BAD_INPUT);
+        if (counts[0xFF] && !(a.esc_enabled && a.esc_code == 0xFFu)) flag(a.status, EQ_DEV_BAD_INPUT);
+    }
+    if (a.esc_enabled && counts[a.esc_code])
+        atomicAdd(reinterpret_cast<unsigned long long *>(at<uint64_t>(a.ws, a.w.misc) + 2),
+                  (unsigned long long)counts[a.esc_code]);
+}
+
+// Quantiser + frequency section (one workgroup of 256 threads per table, one
+// symbol per thread; workgroup 0 also writes the header):
 //   f_s = max(1, floor(c_s * 4096 / N)) for present bytes; a shortfall goes
 //   +1 to the present bytes ranked first by (remainder c_s * 4096 mod N
 //   descending, byte ascending); an excess is taken -1 at a time from the
@@ -188,21 +243,23 @@ __global__ void __launch_bounds__(256) k_enc_quant(EncArgs a) {
     __shared__ int32_t f[256];
     __shared__ int32_t total;
     const uint32_t s = threadIdx.x;
+    const uint64_t g = blockIdx.x;  // table (segment)
+    const uint64_t N = a.n - g * a.seg_syms < a.seg_syms ? a.n - g * a.seg_syms : a.seg_syms;
     __shared__ uint64_t counts[256];  // read by every thread below: staged in LDS
-    const uint64_t c = at<uint64_t>(a.ws, a.w.counts)[s];
+    const uint64_t c = at<uint64_t>(a.ws, a.w.counts)[256 * g + s];
     counts[s] = c;
     const uint64_t scaled = c * (uint64_t)kProbScale;
     const bool present = c != 0;
     int32_t fs = 0;
     if (present) {
-        const uint64_t q = scaled / a.n;
+        const uint64_t q = scaled / N;
         fs = q > 1 ? (int32_t)q : 1;
     }
     f[s] = fs;
     // key = remainder above the byte's complement, so a larger key ranks
     // first; an absent byte's key is 0 and never counts (a strictly larger
     // key is needed)
-    key[s] = present ? ((scaled % a.n) << 8 | (255u - s)) : 0;
+    key[s] = present ? ((scaled % N) << 8 | (255u - s)) : 0;
     if (s == 0) total = 0;
     __syncthreads();
     atomicAdd(&total, fs);
@@ -271,15 +328,7 @@ __global__ void __launch_bounds__(256) k_enc_quant(EncArgs a) {
         cum[s] = v - (uint32_t)f[s];
         __syncthreads();
     }
-    if (s == 0) {
-        // E4M3 NaN codes are only allowed as the escape code; the escape count
-        // must match the list
-        if (a.dtype == EQ_DTYPE_E4M3) {
-            if (counts[0x7F] && !(a.esc_enabled && a.esc_code == 0x7Fu)) flag(a.status, EQ_DEV_BAD_INPUT);
-            if (counts[0xFF] && !(a.esc_enabled && a.esc_code == 0xFFu)) flag(a.status, EQ_DEV_BAD_INPUT);
-        }
-        if (a.esc_enabled ? counts[a.esc_code] != a.n_esc : a.n_esc != 0) flag(a.status, EQ_DEV_BAD_INPUT);
-    }
+    if (s == 0) check_counts(a, counts);
     __syncthreads();
     EncSym es;
     es.rcp = f[s] ? 1.0 / (double)f[s] : 0.0;
@@ -288,34 +337,13 @@ __global__ void __launch_bounds__(256) k_enc_quant(EncArgs a) {
     es.fg = (f[s] < (int32_t)kProbScale ? (uint32_t)f[s] << 4 : 0xFFFFu) |
             ((kProbScale - (uint32_t)f[s]) << 16);
     es.cum = cum[s];
-    at<EncSym>(a.ws, a.w.table)[s] = es;
-    reinterpret_cast<uint16_t *>(a.out + a.sec.freq)[s] = (uint16_t)f[s];
+    at<EncSym>(a.ws, a.w.table)[256 * g + s] = es;
+    reinterpret_cast<uint16_t *>(a.out + a.sec.freq)[256 * g + s] = (uint16_t)f[s];
+    if (g != 0) return;
     // header: every byte written; n_words-dependent fields are filled by k_enc_scan
     if (s < kHeaderBytes / 4) reinterpret_cast<uint32_t *>(a.out)[s] = 0;
     __syncthreads();
-    if (s == 0) {
-        uint8_t *b = a.out;
-        *reinterpret_cast<uint32_t *>(b + H_MAGIC) = kMagic;
-        *reinterpret_cast<uint16_t *>(b + H_VERSION) = kVersion;
-        b[H_DTYPE] = (uint8_t)a.dtype;
-        b[H_FLAGS] = a.esc_enabled ? 1 : 0;
-        *reinterpret_cast<uint64_t *>(b + H_ROWS) = a.rows;
-        *reinterpret_cast<uint64_t *>(b + H_COLS) = a.cols;
-        *reinterpret_cast<uint64_t *>(b + H_N) = a.n;
-        *reinterpret_cast<uint32_t *>(b + H_CHUNK) = a.Z;
-        *reinterpret_cast<uint32_t *>(b + H_LANE_RUN) = a.K;
-        *reinterpret_cast<uint32_t *>(b + H_LANES) = kLanes;
-        *reinterpret_cast<uint32_t *>(b + H_PROB_BITS) = kProbBits;
-        *reinterpret_cast<uint64_t *>(b + H_NCHUNKS) = a.n_chunks;
-        *reinterpret_cast<uint64_t *>(b + H_NESC) = a.n_esc;
-        b[H_ESC_CODE] = a.esc_enabled ? (uint8_t)a.esc_code : 0;
-        *reinterpret_cast<uint64_t *>(b + H_OFF_FREQ) = a.sec.freq;
-        *reinterpret_cast<uint64_t *>(b + H_OFF_SCALES) = a.sec.scales;
-        *reinterpret_cast<uint64_t *>(b + H_OFF_DIR) = a.sec.dir;
-        *reinterpret_cast<uint64_t *>(b + H_OFF_STATES) = a.sec.states;
-        *reinterpret_cast<uint64_t *>(b + H_OFF_WORDS) = a.sec.words;
-        *reinterpret_cast<uint32_t *>(b + H_CODEC) = kCodecRans;
-    }
+    if (s == 0) write_header(a);
 }
 
 // floor(x / f) for 1 <= f <= 4096 and x < f * 2^20 (the state after the
@@ -363,7 +391,9 @@ template <int K>
 __global__ void __launch_bounds__(kEncThreads) k_enc_chunks(EncArgs a) {
     __shared__ __align__(16) EncSym tab[256];
     __shared__ __align__(16) uint16_t rings[kEncWaves][kEncRing];
-    for (uint32_t i = threadIdx.x; i < 256; i += blockDim.x) tab[i] = at<EncSym>(a.ws, a.w.table)[i];
+    // the workgroup's table: its chunks lie in one segment (kEncWaves divides seg)
+    const uint64_t tsel = a.seg ? (uint64_t)blockIdx.x * kEncWaves / a.seg : 0;
+    for (uint32_t i = threadIdx.x; i < 256; i += blockDim.x) tab[i] = at<EncSym>(a.ws, a.w.table)[256 * tsel + i];
     __syncthreads();
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = threadIdx.x >> 6;
@@ -473,7 +503,265 @@ __global__ void __launch_bounds__(kEncThreads) k_enc_chunks(EncArgs a) {
             *reinterpret_cast<uint4 *>(scr + b) = *reinterpret_cast<const uint4 *>(ring + (b & (kEncRing - 1u)));
     }
     at<uint32_t>(a.out, a.sec.states)[k * kLanes + lane] = x;
-    if (lane == 0) at<uint32_t>(a.ws, a.w.wstart)[k] = wpos;
+    if (lane == 0) {
+        at<uint32_t>(a.ws, a.w.wstart)[k] = wpos;
+        at<uint32_t>(a.ws, a.w.wcount)[k] = nk - wpos;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Huffman codec (codec 1): code lengths, canonical codewords, chunk encoder.
+// ---------------------------------------------------------------------------
+
+// Code lengths of at most 12 bits by package-merge, as the host encoder
+// computes them: the present bytes sorted by (count, byte) are the leaves;
+// the list of level d (11 = deepest, 0 = top) is the merge of the leaves
+// with the packages (consecutive pairs) of the list of level d + 1, a leaf
+// first on equal weights; a byte's length is the number of its occurrences
+// among the 2n - 2 first items of the top list and, recursively, the
+// children of the packages among them. The chosen items of every level form
+// a prefix (packages appear in pair order), so level by level only the count
+// of leaves in that prefix is needed. Then the canonical codewords
+// ((length, byte) order), each stored bit-reversed for the LSB-first packing,
+// the length table, the header (one workgroup of 512 threads).
+__global__ void __launch_bounds__(512) k_enc_huff(EncArgs a) {
+    constexpr uint32_t L = kHuffMaxLen;
+    __shared__ uint64_t cnt[256];
+    __shared__ uint64_t leafw[256];   // present counts, ascending (bytes ascending on ties)
+    __shared__ uint32_t leafsym[256];
+    __shared__ uint64_t wbuf[2][512];  // item weights of a level and of the level below
+    __shared__ uint8_t kind[L][512];   // 1: the item is a leaf
+    __shared__ uint32_t mlev[L];       // leaves in each level's chosen prefix
+    __shared__ uint32_t nlen[L + 1];   // codewords of each length
+    __shared__ uint32_t len[256];
+    __shared__ uint32_t npresent;
+    const uint32_t t = threadIdx.x;
+    if (t < 256) {
+        cnt[t] = at<uint64_t>(a.ws, a.w.counts)[t];
+        len[t] = 0;
+    }
+    if (t <= L) nlen[t] = 0;
+    if (t == 0) npresent = 0;
+    __syncthreads();
+    if (t == 0) check_counts(a, cnt);
+    if (t < 256 && cnt[t]) {
+        const uint64_t ct = cnt[t];
+        uint32_t r = 0;
+        for (uint32_t u = 0; u < 256; ++u) {
+            const uint64_t cu = cnt[u];
+            r += (cu && (cu < ct || (cu == ct && u < t))) ? 1u : 0u;
+        }
+        leafw[r] = ct;
+        leafsym[r] = t;
+        atomicAdd(&npresent, 1u);
+    }
+    __syncthreads();
+    const uint32_t n = npresent;
+    uint32_t *hs = at<uint32_t>(a.ws, a.w.table);  // [256] reversed code | length << 16, [256] lone flag
+    if (n == 1) {
+        // one byte: a zero-bit code, no words at all
+        if (t < 256) {
+            hs[t] = 0;
+            reinterpret_cast<uint16_t *>(a.out + a.sec.freq)[t] = cnt[t] ? kHuffZero : 0;
+        }
+        if (t == 0) hs[256] = 1;
+    } else {
+        uint32_t below = 0;  // size of the level below
+        for (int d = (int)L - 1; d >= 0; --d) {
+            const uint64_t *deep = wbuf[(d + 1) & 1];
+            uint64_t *cur = wbuf[d & 1];
+            const uint32_t packs = below / 2;
+            if (t < n) {  // leaf t: after the packages lighter than it
+                const uint64_t w = leafw[t];
+                uint32_t lo = 0, hi = packs;
+                while (lo < hi) {
+                    const uint32_t mid = (lo + hi) / 2;
+                    if (deep[2 * mid] + deep[2 * mid + 1] < w) lo = mid + 1;
+                    else hi = mid;
+                }
+                cur[t + lo] = w;
+                kind[d][t + lo] = 1;
+            }
+            if (t < packs) {  // package t: after the leaves not heavier than it
+                const uint64_t pw = deep[2 * t] + deep[2 * t + 1];
+                uint32_t lo = 0, hi = n;
+                while (lo < hi) {
+                    const uint32_t mid = (lo + hi) / 2;
+                    if (leafw[mid] <= pw) lo = mid + 1;
+                    else hi = mid;
+                }
+                cur[t + lo] = pw;
+                kind[d][t + lo] = 0;
+            }
+            below = n + packs;
+            __syncthreads();
+        }
+        // chosen prefixes, top down
+        uint32_t P = 2 * n - 2;
+        for (uint32_t d = 0; d < L; ++d) {
+            const uint32_t leaves = (uint32_t)__syncthreads_count(t < P && kind[d][t]);
+            if (t == 0) mlev[d] = leaves;
+            P = 2 * (P - leaves);
+        }
+        __syncthreads();
+        if (t < n) {
+            uint32_t l = 0;
+            for (uint32_t d = 0; d < L; ++d) l += t < mlev[d] ? 1u : 0u;
+            len[leafsym[t]] = l;
+            atomicAdd(&nlen[l], 1u);
+        }
+        __syncthreads();
+        if (t < 256) {
+            const uint32_t l = len[t];
+            uint32_t code = 0;
+            if (l) {
+                // first codeword of length l, then the rank among its bytes
+                uint32_t c = 0;
+                for (uint32_t j = 1; j < l; ++j) c = (c + nlen[j]) << 1;
+                uint32_t r = 0;
+                for (uint32_t u = 0; u < t; ++u) r += len[u] == l ? 1u : 0u;
+                code = c + r;
+            }
+            hs[t] = l ? (__builtin_bitreverse32(code) >> (32u - l)) | (l << 16) : 0u;
+            reinterpret_cast<uint16_t *>(a.out + a.sec.freq)[t] = (uint16_t)l;
+        }
+        if (t == 0) hs[256] = 0;
+    }
+    if (t < kHeaderBytes / 4) reinterpret_cast<uint32_t *>(a.out)[t] = 0;
+    __syncthreads();
+    if (t == 0) write_header(a);
+}
+
+constexpr uint32_t kHuffAhead = 28;  // steps a lane's stream is packed ahead of the decoder replay
+constexpr uint32_t kEntRow = 66;     // u16 per lane row of the 64-step entry ring (+2: fewer bank conflicts)
+constexpr uint32_t kWordRow = 33;    // u16 per lane row of the 32-word stream ring
+
+// One wave per chunk, steps walked forwards, replaying the decoder: at each
+// step a lane holding (decoder side) fewer than 12 bits takes its next
+// 16-bit word, ascending lanes in one step taking consecutive slots (ballot
+// + mbcnt). Every lane packs its own codeword stream (codewords from bit 0
+// up, each first bit first) 28 steps ahead of the replay, one codeword per
+// step, into a 32-word LDS ring; the word a lane takes is always complete
+// by then: when it needs one it holds < 12 bits, so the 16 bits it takes
+// end within its next 28 codewords (each at least one bit), and a lane's
+// unused packed bits stay below 28 * 12 + 16. At the stream's end the
+// partial last word is packed zero-padded, and a lane asking for more gets
+// zero words. The symbols' (reversed codeword, length) entries of the next
+// steps are staged in a per-lane 64-step LDS ring, their bytes loaded about
+// 32 steps before they are staged. Words leave through the LDS output ring
+// as in the rANS encoder, filled from the chunk's start.
+template <int K>
+__global__ void __launch_bounds__(kEncThreads) k_enc_hchunks(EncArgs a) {
+    __shared__ uint32_t hs[257];
+    __shared__ __align__(16) uint16_t entring[kEncWaves][64 * kEntRow];
+    __shared__ __align__(16) uint16_t wordring[kEncWaves][64 * kWordRow];
+    __shared__ __align__(16) uint16_t rings[kEncWaves][kEncRing];
+    for (uint32_t i = threadIdx.x; i < 257; i += blockDim.x) hs[i] = at<uint32_t>(a.ws, a.w.table)[i];
+    __syncthreads();
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = threadIdx.x >> 6;
+    const uint64_t k = (uint64_t)blockIdx.x * kEncWaves + wave;
+    if (k >= a.n_chunks) return;
+    const uint64_t p0 = k * a.Z;
+    const uint32_t nk = (uint32_t)(a.n - p0 < a.Z ? a.n - p0 : a.Z);
+    uint32_t words = 0;
+    if (hs[256] == 0) {
+        const uint8_t *sym = a.sym + p0;
+        uint16_t *scr = at<uint16_t>(a.ws, a.w.scratch) + p0;
+        uint16_t *ring = rings[wave];
+        uint16_t *er = &entring[wave][lane * kEntRow];
+        uint16_t *wr = &wordring[wave][lane * kWordRow];
+        constexpr uint32_t G = 64u * K;
+        constexpr int W = (K + 3) / 4;
+        // groups staged ahead of the one being replayed (at least 28 steps),
+        // and loads in flight (about 32 steps ahead of their staging)
+        constexpr uint32_t DELTA = (kHuffAhead + K - 1) / K;
+        constexpr uint32_t P = K >= 8 ? 4u : 32u / K;
+        static_assert((DELTA + 1) * K <= 64, "entry ring");
+        const uint32_t groups = (nk + G - 1) / G;
+        const uint32_t T = groups * K;
+        auto pos = [&](uint32_t st) { return (st / K) * G + lane * K + (st % K); };
+        // entries: reversed codeword | length << 12
+        auto stage_group = [&](uint32_t g, const uint32_t (&w)[W]) {
+            if (g >= groups) return;
+#pragma unroll
+            for (int i = 0; i < K; ++i) {
+                const uint32_t e = hs[(w[i / 4] >> (8 * (i % 4))) & 0xFFu];
+                er[(g * K + i) & 63u] = (uint16_t)((e & 0xFFFu) | ((e >> 16) << 12));
+            }
+        };
+        uint32_t acc = 0, ab = 0;      // packed bits not yet in a word, their count
+        uint32_t wprod = 0, wnext = 0; // words packed; the next one to hand out
+        bool ended = false;            // the stream is fully packed
+        // branch-free: past the stream's end the entry reads as 0 bits, and
+        // the first such step flushes the partial word
+        auto pack = [&](uint32_t st) {
+            const bool valid = st < T && pos(st) < nk;
+            const uint32_t e0 = er[st & 63u];
+            const uint32_t e = valid ? e0 : 0u;
+            acc |= (e & 0xFFFu) << ab;
+            ab += e >> 12;
+            const bool emit = ab >= 16 || (!valid && !ended && ab != 0);
+            if (emit) wr[wprod & 31u] = (uint16_t)acc;
+            wprod += emit ? 1u : 0u;
+            acc = emit ? acc >> 16 : acc;
+            ab = emit ? (ab >= 16 ? ab - 16 : 0u) : ab;
+            ended = ended || !valid;
+        };
+        // the first DELTA groups staged directly, the next P in flight
+        for (uint32_t g = 0; g < DELTA && g < groups; ++g) {
+            uint32_t w[W];
+            load_run<K>(sym, g * G + lane * K, nk, w);
+            stage_group(g, w);
+        }
+        uint32_t q[P][W];
+#pragma unroll
+        for (uint32_t d = 0; d < P; ++d)
+            if (DELTA + d < groups) load_run<K>(sym, (DELTA + d) * G + lane * K, nk, q[d]);
+        for (uint32_t st = 0; st < kHuffAhead; ++st) pack(st);
+        uint32_t held = 0;                    // the decoder's bits at this step
+        uint32_t ptr = 0, flushed = 0;        // words written; words already in the scratch
+        for (uint32_t g0 = 0; g0 < groups; g0 += P) {
+#pragma unroll
+            for (uint32_t d = 0; d < P; ++d) {
+                const uint32_t g = g0 + d;
+                if (g >= groups) break;
+                // q[d] holds group g + DELTA: stage it, then load group g + DELTA + P
+                stage_group(g + DELTA, q[d]);
+                if (g + DELTA + P < groups) load_run<K>(sym, (g + DELTA + P) * G + lane * K, nk, q[d]);
+#pragma unroll
+                for (uint32_t i = 0; i < K; ++i) {
+                    const uint32_t t = g * K + i;
+                    pack(t + kHuffAhead);
+                    const bool active = pos(t) < nk;
+                    const bool need = active && held < 12;
+                    const uint64_t m = __builtin_amdgcn_ballot_w64(need);
+                    const uint32_t slot = __builtin_amdgcn_mbcnt_hi(
+                        (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, ptr));
+                    const uint16_t w0 = wr[wnext & 31u];
+                    const uint32_t len = er[t & 63u] >> 12;
+                    if (need) ring[slot & (kEncRing - 1u)] = wnext < wprod ? w0 : (uint16_t)0;
+                    wnext += need ? 1u : 0u;
+                    held = held + (need ? 16u : 0u) - (active ? len : 0u);
+                    ptr += (uint32_t)__builtin_popcountll(m);
+                }
+                while (ptr >= flushed + kEncFlush) {
+                    const uint32_t b = flushed + lane * 8u;
+                    *reinterpret_cast<uint4 *>(scr + b) =
+                        *reinterpret_cast<const uint4 *>(ring + (b & (kEncRing - 1u)));
+                    flushed += kEncFlush;
+                }
+            }
+        }
+        // the last words (the rest of their 8-word block is scratch nobody reads)
+        const uint32_t b = flushed + lane * 8u;
+        if (b < ptr) *reinterpret_cast<uint4 *>(scr + b) = *reinterpret_cast<const uint4 *>(ring + (b & (kEncRing - 1u)));
+        words = ptr;
+    }
+    if (lane == 0) {
+        at<uint32_t>(a.ws, a.w.wstart)[k] = 0;
+        at<uint32_t>(a.ws, a.w.wcount)[k] = words;
+    }
 }
 
 // Directory, n_words and the offsets that follow the words (one workgroup).
@@ -483,14 +771,13 @@ __global__ void __launch_bounds__(1024) k_enc_scan(EncArgs a) {
     const uint32_t t = threadIdx.x;
     if (t == 0) carry = 0;
     __syncthreads();
-    const uint32_t *wstart = at<uint32_t>(a.ws, a.w.wstart);
+    const uint32_t *wcount = at<uint32_t>(a.ws, a.w.wcount);
     uint64_t *first = at<uint64_t>(a.ws, a.w.first);
     for (uint64_t base = 0; base < a.n_chunks; base += 1024) {
         const uint64_t k = base + t;
         uint64_t cnt = 0, padded = 0;
         if (k < a.n_chunks) {
-            const uint32_t nk = (uint32_t)(a.n - k * a.Z < a.Z ? a.n - k * a.Z : a.Z);
-            cnt = nk - wstart[k];
+            cnt = wcount[k];
             padded = round_up(cnt, kWordPad);
         }
         part[t] = padded;
@@ -527,6 +814,8 @@ __global__ void __launch_bounds__(1024) k_enc_scan(EncArgs a) {
         misc[0] = n_words;
         misc[1] = total;
         if (a.out_len) *a.out_len = total;
+        // the escape codes counted by the table kernels against the list
+        if (misc[2] != (a.esc_enabled ? a.n_esc : 0)) flag(a.status, EQ_DEV_BAD_INPUT);
     }
 }
 
@@ -565,9 +854,8 @@ __global__ void __launch_bounds__(kEncThreads) k_enc_copy(EncArgs a) {
     const uint64_t k = (uint64_t)blockIdx.x * kEncWaves + (threadIdx.x >> 6);
     if (k < a.n_chunks) {
         const uint64_t p0 = k * a.Z;
-        const uint32_t nk = (uint32_t)(a.n - p0 < a.Z ? a.n - p0 : a.Z);
         const uint32_t ws = at<uint32_t>(a.ws, a.w.wstart)[k];
-        const uint32_t cnt = nk - ws;
+        const uint32_t cnt = at<uint32_t>(a.ws, a.w.wcount)[k];
         const uint32_t nblk = (uint32_t)round_up(cnt, kWordPad) / 8u;
         const uint32_t s = ws & 7u;
         const uint4 *src = reinterpret_cast<const uint4 *>(at<uint16_t>(a.ws, a.w.scratch) + p0 + (ws - s));
@@ -625,7 +913,8 @@ __global__ void __launch_bounds__(kEncThreads) k_enc_copy(EncArgs a) {
 
 template <int K>
 void launch_chunks(uint32_t grid, hipStream_t s, const EncArgs &a) {
-    hipLaunchKernelGGL(k_enc_chunks<K>, dim3(grid), dim3(kEncThreads), 0, s, a);
+    if (a.codec == kCodecHuffman) hipLaunchKernelGGL(k_enc_hchunks<K>, dim3(grid), dim3(kEncThreads), 0, s, a);
+    else hipLaunchKernelGGL(k_enc_chunks<K>, dim3(grid), dim3(kEncThreads), 0, s, a);
 }
 
 }  // namespace
@@ -636,7 +925,8 @@ uint64_t eq_encode_device_bound(uint64_t rows, uint64_t cols, uint32_t chunk_sym
     if (rows == 0 || cols == 0 || chunk_symbols == 0 || cols > (1ull << 40) / rows) return 0;
     const uint64_t n = rows * cols;
     const uint64_t n_chunks = (n + chunk_symbols - 1) / chunk_symbols;
-    return layout(rows, n_chunks, n + kWordPad * n_chunks, n_esc).total;
+    // the largest variant: rANS lane states and the most tables
+    return layout(rows, n_chunks, n + kWordPad * n_chunks, n_esc, kCodecRans, max_tables(n_chunks)).total;
 }
 
 uint64_t eq_encode_device_workspace(uint64_t rows, uint64_t cols, uint32_t chunk_symbols) {
@@ -651,7 +941,10 @@ eq_status eq_encode_device(const eq_tensor_desc *d, const uint8_t *d_symbols, co
                            uint64_t *d_out_len, uint32_t *d_status, void *stream) {
     if (!d || !d_symbols || !d_scales || !d_workspace || !d_out) return EQ_EINVAL;
     if (n_esc && (!d_esc_idx || !d_esc_bf16)) return EQ_EINVAL;
-    if (d->codec != kCodecRans || d->seg_chunks) return EQ_EUNSUPPORTED;
+    if (d->codec != kCodecRans && d->codec != kCodecHuffman) return EQ_EINVAL;
+    // adaptive tables: a multiple of 8 chunks per table, rANS only
+    if (d->seg_chunks && (d->seg_chunks % 8 || d->codec != kCodecRans)) return EQ_EINVAL;
+    if (d->reserved) return EQ_EINVAL;
     if (d->dtype != EQ_DTYPE_INT8 && d->dtype != EQ_DTYPE_E4M3) return EQ_EINVAL;
     if (d->rows == 0 || d->cols == 0 || d->cols > (1ull << 40) / d->rows) return EQ_EINVAL;
     if (!valid_lane_run(d->lane_run)) return EQ_EINVAL;
@@ -686,18 +979,27 @@ eq_status eq_encode_device(const eq_tensor_desc *d, const uint8_t *d_symbols, co
     a.dtype = d->dtype;
     a.esc_enabled = d->esc_enabled;
     a.esc_code = d->esc_code;
+    a.codec = d->codec;
+    a.seg = d->seg_chunks;
+    a.n_tab = n_tables(n_chunks, a.seg);
+    a.seg_syms = a.seg ? (uint64_t)a.seg * Z : n;
     a.w = w;
-    a.sec = layout(d->rows, n_chunks, 0, 0);  // fields before the words do not depend on the counts
+    // fields before the words do not depend on the counts
+    a.sec = layout(d->rows, n_chunks, 0, 0, a.codec, a.n_tab);
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const uint32_t cgrid = (uint32_t)((n_chunks + kEncWaves - 1) / kEncWaves);
     if (n_chunks > 0xFFFFFFFFull / 4) return EQ_EINVAL;
     hipLaunchKernelGGL(k_enc_check, dim3(64), dim3(256), 0, s, a);
-    // about 32 KiB of symbols per workgroup and pass, at most kHistMaxGrid workgroups
-    const uint64_t hg = (n + 32767) / 32768;
-    const uint32_t hgrid = (uint32_t)(hg < kHistMaxGrid ? (hg ? hg : 1) : kHistMaxGrid);
-    hipLaunchKernelGGL(k_enc_hist, dim3(hgrid), dim3(256), 0, s, a);
-    hipLaunchKernelGGL(k_enc_quant, dim3(1), dim3(256), 0, s, a);
+    // one grid row per table; about 32 KiB of symbols per workgroup and pass,
+    // at most kHistMaxGrid workgroups in all (and at least one per table)
+    const uint64_t hg = (a.seg_syms + 32767) / 32768;
+    const uint64_t hcap = kHistMaxGrid / a.n_tab ? kHistMaxGrid / a.n_tab : 1;
+    const uint32_t hgrid = (uint32_t)(hg < hcap ? (hg ? hg : 1) : hcap);
+    if (a.n_tab > 65535) return EQ_EINVAL;
+    hipLaunchKernelGGL(k_enc_hist, dim3(hgrid, (uint32_t)a.n_tab), dim3(256), 0, s, a);
+    if (a.codec == kCodecHuffman) hipLaunchKernelGGL(k_enc_huff, dim3(1), dim3(512), 0, s, a);
+    else hipLaunchKernelGGL(k_enc_quant, dim3((uint32_t)a.n_tab), dim3(256), 0, s, a);
     switch (K) {
         case 1: launch_chunks<1>(cgrid, s, a); break;
         case 2: launch_chunks<2>(cgrid, s, a); break;

@@ -345,7 +345,8 @@ EQ_DEV_BAD_INPUT = 4
 
 def eq_encode_device(dtype: int, rows: int, cols: int, d_symbols, d_scales, d_esc_idx=None,
                      d_esc_val=None, esc_code: int = 0, chunk_symbols: int = 65536, lane_run: int = 8,
-                     workspace=None, out=None, stream=None, d_len=None, d_status=None):
+                     workspace=None, out=None, stream=None, d_len=None, d_status=None,
+                     codec: int = 0, seg_chunks: int = 0):
     """Device-side encode (torch tensors on the GPU). Returns (out, d_len,
     d_status) without synchronising: out[:int(d_len)] is the container once
     the stream has run. A d_status passed in is not cleared (flags of
@@ -354,7 +355,7 @@ def eq_encode_device(dtype: int, rows: int, cols: int, d_symbols, d_scales, d_es
     n_esc = 0 if d_esc_idx is None else int(d_esc_idx.numel())
     d = eq_tensor_desc(dtype=dtype, lane_run=lane_run, rows=rows, cols=cols,
                        chunk_symbols=chunk_symbols, esc_enabled=1 if n_esc or esc_code else 0,
-                       esc_code=esc_code, codec=EQ_CODEC_RANS)
+                       esc_code=esc_code, codec=codec, seg_chunks=seg_chunks)
     dev = d_symbols.device
     wsb = int(_lib.eq_encode_device_workspace(rows, cols, chunk_symbols))
     cap = int(_lib.eq_encode_device_bound(rows, cols, chunk_symbols, n_esc))

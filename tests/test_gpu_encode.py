@@ -19,29 +19,32 @@ def _dev(a, dtype):
     return torch.from_numpy(np.ascontiguousarray(a)).to("cuda") if a is not None else None
 
 
-def device_container(sym, scales, dtype, rows, cols, Z, K, esc_idx=None, esc_val=None, esc_code=0):
+def device_container(sym, scales, dtype, rows, cols, Z, K, esc_idx=None, esc_val=None, esc_code=0,
+                     codec=0, seg=0):
     ds = _dev(sym, None)
     dsc = _dev(scales.astype(np.float32), None)
     di = _dev(esc_idx.astype(np.int64), None) if esc_idx is not None and len(esc_idx) else None
     dv = _dev(esc_val.view(np.int16), None) if esc_val is not None and len(esc_val) else None
-    out, d_len, st = eq.eq_encode_device(dtype, rows, cols, ds, dsc, di, dv, esc_code, Z, K)
+    out, d_len, st = eq.eq_encode_device(dtype, rows, cols, ds, dsc, di, dv, esc_code, Z, K,
+                                         codec=codec, seg_chunks=seg)
     torch.cuda.synchronize()
     n = int(d_len.item())
     return out[:n].cpu().numpy(), int(st.item())
 
 
-def host_container(sym, scales, dtype, rows, cols, Z, K, esc_idx=None, esc_val=None, esc_code=0):
-    return eq.encode_host(eq.build_tables(sym), dtype, rows, cols, sym, scales,
+def host_container(sym, scales, dtype, rows, cols, Z, K, esc_idx=None, esc_val=None, esc_code=0,
+                   codec=0, seg=0):
+    return eq.encode_host(None if seg else eq.build_tables(sym), dtype, rows, cols, sym, scales,
                           esc_idx if esc_idx is not None and len(esc_idx) else None,
                           esc_val if esc_val is not None and len(esc_val) else None,
-                          esc_code=esc_code, chunk_symbols=Z, lane_run=K)
+                          esc_code=esc_code, chunk_symbols=Z, lane_run=K, codec=codec, seg_chunks=seg)
 
 
 def check_equal(sym, scales, dtype, rows, cols, Z=65536, K=8, esc_idx=None, esc_val=None, esc_code=0,
-                what=""):
-    got, st = device_container(sym, scales, dtype, rows, cols, Z, K, esc_idx, esc_val, esc_code)
+                what="", codec=0, seg=0):
+    got, st = device_container(sym, scales, dtype, rows, cols, Z, K, esc_idx, esc_val, esc_code, codec, seg)
     assert st == 0, f"{what}: device status {st}"
-    exp = host_container(sym, scales, dtype, rows, cols, Z, K, esc_idx, esc_val, esc_code)
+    exp = host_container(sym, scales, dtype, rows, cols, Z, K, esc_idx, esc_val, esc_code, codec, seg)
     assert got.size == exp.size, f"{what}: size {got.size} vs {exp.size}"
     bad = np.flatnonzero(got != exp)
     assert bad.size == 0, f"{what}: {bad.size} bytes differ, first at {bad[0]}"
@@ -122,3 +125,93 @@ def test_bad_inputs_raise_the_device_flag():
     sym2[5] = 0x7F
     _, st = device_container(sym2, np.ones(4, np.float32), 2, 4, 1024, 4096, 8)
     assert st & eq.EQ_DEV_BAD_INPUT  # E4M3 NaN code, not an escape
+
+
+# --- the Huffman codec and adaptive (per-segment) tables -------------------
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_huffman_config_matrices(cfg):
+    t = synth.make_tensor(cfg, 0, 0)
+    sp = t.spec
+    log(f"case device Huffman encode config {cfg}")
+    c = check_equal(t.symbols, t.scales, sp.dtype, sp.rows, sp.cols, what=f"huffman config {cfg}",
+                    codec=eq.EQ_CODEC_HUFFMAN)
+    sym, st = run_u8([eq.DeviceContainer(c, device="cuda")], sp.n)
+    assert st == 0
+    assert_same(sym, t.symbols, "round trip")
+
+
+def test_huffman_block_tensors_with_escapes_and_e4m3():
+    for cfg, i in [(4, 6), (4, 1), (3, 0)]:
+        t = synth.make_tensor(cfg, 0, i)
+        sp = t.spec
+        log(f"case device Huffman encode config {cfg} tensor {sp.name}")
+        esc = t.esc_idx.size > 0
+        check_equal(t.symbols, t.scales, sp.dtype, sp.rows, sp.cols,
+                    esc_idx=t.esc_idx if esc else None, esc_val=t.esc_val if esc else None,
+                    esc_code=t.esc_code if esc else 0, what=f"huffman cfg {cfg} {sp.name}",
+                    codec=eq.EQ_CODEC_HUFFMAN)
+        del t
+
+
+def test_huffman_random_layouts_and_one_symbol():
+    rng = np.random.default_rng(41)
+    for it in range(60):
+        K = int(rng.choice([1, 2, 4, 8, 16]))
+        Z = 64 * K * int(rng.integers(1, 9))
+        n = int(rng.integers(1, 5 * Z))
+        n = max(16, n - n % 16) if it % 2 else n
+        # every tenth layout near-uniform over all 256 codes; every seventh one code
+        k = 256 if it % 10 == 9 else (1 if it % 7 == 3 else int(rng.integers(2, 60)))
+        present = rng.choice(256, size=k, replace=False)
+        w = rng.uniform(0.5, 1.0, k) if k == 256 else rng.exponential(1.0, k) ** 3 + 1e-6
+        sym = present[rng.choice(k, size=n, p=w / w.sum())].astype(np.uint8)
+        divs = [d for d in range(1, min(n, 64) + 1) if n % d == 0]
+        rows = int(rng.choice(divs))
+        scales = rng.uniform(-2, 2, rows).astype(np.float32)
+        check_equal(sym, scales, 1, rows, n // rows, Z, K, what=f"huffman random {it} K={K} Z={Z} n={n} k={k}",
+                    codec=eq.EQ_CODEC_HUFFMAN)
+
+
+def test_adaptive_tables_random_layouts():
+    rng = np.random.default_rng(43)
+    for it in range(40):
+        K = int(rng.choice([1, 4, 8, 16]))
+        Z = 64 * K * int(rng.integers(1, 5))
+        seg = int(rng.choice([8, 16, 24]))
+        n = int(rng.integers(1, 3 * seg * Z))
+        # drifting distributions: each quarter of the tensor draws from its own codes
+        parts = []
+        for q in range(4):
+            k = int(rng.integers(1, 40))
+            present = rng.choice(256, size=k, replace=False)
+            w = rng.exponential(1.0, k) ** 3 + 1e-6
+            m = n // 4 + (n % 4 if q == 3 else 0)
+            parts.append(present[rng.choice(k, size=m, p=w / w.sum())].astype(np.uint8))
+        sym = np.concatenate(parts)
+        divs = [d for d in range(1, min(n, 64) + 1) if n % d == 0]
+        rows = int(rng.choice(divs))
+        scales = rng.uniform(-2, 2, rows).astype(np.float32)
+        check_equal(sym, scales, 1, rows, n // rows, Z, K, what=f"segments {it} K={K} Z={Z} seg={seg} n={n}",
+                    seg=seg)
+
+
+def test_adaptive_tables_drifting_tensor_round_trip():
+    t = synth.drift_tensor(1024, 8192, seed=3)
+    log("case device encode drifting tensor, 8-chunk tables")
+    c = check_equal(t.symbols, t.scales, t.spec.dtype, t.spec.rows, t.spec.cols, what="drift seg 8", seg=8)
+    sym, st = run_u8([eq.DeviceContainer(c, device="cuda")], t.spec.n)
+    assert st == 0
+    assert_same(sym, t.symbols, "round trip")
+
+
+def test_codec_and_segment_argument_errors():
+    sym = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    sc = torch.ones(4, dtype=torch.float32, device="cuda")
+    with pytest.raises(eq.EqError):
+        eq.eq_encode_device(1, 4, 1024, sym, sc, chunk_symbols=512, lane_run=8,
+                            codec=eq.EQ_CODEC_HUFFMAN, seg_chunks=8)  # adaptive tables are rANS only
+    with pytest.raises(eq.EqError):
+        eq.eq_encode_device(1, 4, 1024, sym, sc, chunk_symbols=512, lane_run=8, seg_chunks=4)  # not a multiple of 8
+    with pytest.raises(eq.EqError):
+        eq.eq_encode_device(1, 4, 1024, sym, sc, chunk_symbols=512, lane_run=8, codec=7)
