@@ -214,8 +214,10 @@ __device__ __forceinline__ void build_lut(const uint16_t *freq, LutEnt *lut, uin
     // bytes have increasing cum). Each thread owns P consecutive slots.
     constexpr uint32_t P = 4096u / kThreads;
     static_assert(P * kThreads == 4096u, "slots per thread");
-    uint32_t *wmax = scr + 260;                                     // [kWaves]
-    uint16_t *mark = reinterpret_cast<uint16_t *>(scr + 272);       // [4096]
+    uint32_t *wmax = scr + 260;  // [kWaves]
+    // the marks live in the table's own memory: every thread reads its marks
+    // before the barrier that precedes the first table write
+    uint16_t *mark = reinterpret_cast<uint16_t *>(lut);  // [4096]
 #pragma unroll
     for (uint32_t j = 0; j < P; ++j) mark[P * tid + j] = 0;
     __syncthreads();
@@ -949,8 +951,8 @@ __global__ void __launch_bounds__(kThreads) k_decode(LArgs a) {
     constexpr bool GEMV = OUT == OUT_GEMV;
     __shared__ LutEnt lut[4096];
     __shared__ __attribute__((aligned(16))) uint16_t rings[kWaves][kRingAlloc];
-    // the slot-table build's scratch (cum, wave maxima, 4096 u16 marks) lives in the rings
-    static_assert(!EQ_LUT_SCAN || sizeof(rings) >= 272 * 4 + 4096 * 2, "rings too small for the table build");
+    // the slot-table build's scratch (cum, wave maxima) lives in the rings
+    static_assert(sizeof(rings) >= (260 + kWaves) * 4, "rings too small for the table build");
 
     const uint32_t wg = blockIdx.x;
     uint32_t ti = 0;
