@@ -725,7 +725,7 @@ __global__ void __launch_bounds__(kEncThreads) k_enc_hchunks(EncArgs a) {
 #pragma unroll
             for (uint32_t d = 0; d < P; ++d) {
                 const uint32_t g = g0 + d;
-                if (g >= groups) break;
+                if (g >= groups) continue;  // (the rest of this batch is past the chunk)
                 // q[d] holds group g + DELTA: stage it, then load group g + DELTA + P
                 stage_group(g + DELTA, q[d]);
                 if (g + DELTA + P < groups) load_run<K>(sym, (g + DELTA + P) * G + lane * K, nk, q[d]);
