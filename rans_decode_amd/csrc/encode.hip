@@ -218,6 +218,28 @@ __device__ __forceinline__ void write_header(const EncArgs &a) {
     *reinterpret_cast<uint32_t *>(b + H_SEG) = a.seg;
 }
 
+// Sum, maximum and minimum over a 256-thread workgroup (every thread calls
+// them; red holds 4 ints): a shuffle butterfly per wave, then the four wave
+// results.
+template <typename Op>
+__device__ __forceinline__ int32_t block_reduce256(int32_t v, int32_t *red, Op op) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = op(v, __shfl_xor(v, o, 64));
+    __syncthreads();  // the previous call's readers are done with red
+    if ((threadIdx.x & 63u) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    return op(op(red[0], red[1]), op(red[2], red[3]));
+}
+__device__ __forceinline__ int32_t block_sum256(int32_t v, int32_t *red) {
+    return block_reduce256(v, red, [](int32_t x, int32_t y) { return x + y; });
+}
+__device__ __forceinline__ int32_t block_max256(int32_t v, int32_t *red) {
+    return block_reduce256(v, red, [](int32_t x, int32_t y) { return x > y ? x : y; });
+}
+__device__ __forceinline__ int32_t block_min256(int32_t v, int32_t *red) {
+    return block_reduce256(v, red, [](int32_t x, int32_t y) { return x < y ? x : y; });
+}
+
 // Per-table checks (thread 0): E4M3 NaN codes only as the escape code; the
 // escape codes seen are summed for k_enc_scan, which compares the total with
 // the list.
@@ -239,9 +261,9 @@ __device__ __forceinline__ void check_counts(const EncArgs &a, const uint64_t *c
 //   largest f_s > 1 (smallest byte among equals), computed here in closed
 //   form.
 __global__ void __launch_bounds__(256) k_enc_quant(EncArgs a) {
-    __shared__ uint64_t key[256];
-    __shared__ int32_t f[256];
-    __shared__ int32_t total;
+    __shared__ __align__(16) uint64_t key[256];
+    __shared__ __align__(16) int32_t f[256];
+    __shared__ int32_t red[4];
     const uint32_t s = threadIdx.x;
     const uint64_t g = blockIdx.x;  // table (segment)
     const uint64_t N = a.n - g * a.seg_syms < a.seg_syms ? a.n - g * a.seg_syms : a.seg_syms;
@@ -260,19 +282,19 @@ __global__ void __launch_bounds__(256) k_enc_quant(EncArgs a) {
     // first; an absent byte's key is 0 and never counts (a strictly larger
     // key is needed)
     key[s] = present ? ((scaled % N) << 8 | (255u - s)) : 0;
-    if (s == 0) total = 0;
-    __syncthreads();
-    atomicAdd(&total, fs);
-    __syncthreads();
-    const int32_t deficit = (int32_t)kProbScale - total;
+    const int32_t deficit = (int32_t)kProbScale - block_sum256(fs, red);
     if (deficit > 0) {
         if (present) {
             // rank among present bytes by (remainder descending, byte
             // ascending): one branch-free u64 key compare per byte
             uint32_t rank = 0;
             const uint64_t ks = key[s];
-#pragma unroll 16
-            for (uint32_t t = 0; t < 256; ++t) rank += key[t] > ks ? 1u : 0u;
+            const ulonglong2 *k2 = reinterpret_cast<const ulonglong2 *>(key);
+#pragma unroll 8
+            for (uint32_t q = 0; q < 128; ++q) {  // 16-byte reads, many in flight
+                const ulonglong2 w = k2[q];
+                rank += (w.x > ks ? 1u : 0u) + (w.y > ks ? 1u : 0u);
+            }
             if ((int32_t)rank < deficit) f[s] = fs + 1;
         }
         __syncthreads();
@@ -283,32 +305,39 @@ __global__ void __launch_bounds__(256) k_enc_quant(EncArgs a) {
         // down to v and the remaining E - cost(v) decrements go to the
         // bytes then at v in ascending order (each leaves the top level
         // after its one decrement). v = 1 would mean too few f > 1.
+        // E <= 256 (each present byte's f is rounded up by less than 2), and
+        // v lies in (max f - E, max f] (the largest f alone costs E at
+        // max f - E): thread u tests the level max f - u.
         const int32_t E = -deficit;
-        __shared__ int32_t acc;
-        auto cost = [&](int32_t v) {  // every thread calls it
-            __syncthreads();
-            if (s == 0) acc = 0;
-            __syncthreads();
-            if (fs > v) atomicAdd(&acc, fs - v);
-            __syncthreads();
-            return acc;
-        };
-        int32_t lo = 1, hi = (int32_t)kProbScale;  // cost(hi) = 0 < E
-        while (lo < hi) {
-            const int32_t mid = (lo + hi) / 2;
-            if (cost(mid) < E) hi = mid;
-            else lo = mid + 1;
+        const int32_t top = block_max256(fs, red);
+        int32_t cand = 0x7FFFFFFF;
+        const int32_t level = top - (int32_t)s;
+        if ((int32_t)s < E && level >= 1) {
+            int32_t c = 0;
+            const int4 *f4 = reinterpret_cast<const int4 *>(f);
+#pragma unroll 8
+            for (uint32_t q = 0; q < 64; ++q) {  // 16-byte reads, many in flight
+                const int4 w = f4[q];
+                c += (w.x > level ? w.x - level : 0) + (w.y > level ? w.y - level : 0) +
+                     (w.z > level ? w.z - level : 0) + (w.w > level ? w.w - level : 0);
+            }
+            if (c < E) cand = level;
         }
-        const int32_t v = lo;
+        const int32_t v = block_min256(cand, red);
         if (v == 1) {
             if (s == 0) flag(a.status, EQ_DEV_BAD_INPUT);
         } else {
-            const int32_t r = E - cost(v);
-            uint32_t rank = 0;  // bytes below s at the top level after the cut
-#pragma unroll 16
-            for (uint32_t t = 0; t < 256; ++t) rank += (t < s && f[t] >= v) ? 1u : 0u;
+            const int32_t r = E - block_sum256(fs > v ? fs - v : 0, red);
+            // bytes below s at the top level after the cut: the ballot's
+            // lanes below s plus the earlier waves' counts
+            const bool at_top = fs >= v;
+            const uint64_t m = __builtin_amdgcn_ballot_w64(at_top);
+            __shared__ uint32_t wcnt[4];
+            if ((s & 63u) == 0) wcnt[s >> 6] = (uint32_t)__builtin_popcountll(m);
             __syncthreads();
-            if (fs >= v) f[s] = v - ((int32_t)rank < r ? 1 : 0);
+            uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            for (uint32_t w = 0; w < (s >> 6); ++w) rank += wcnt[w];
+            if (at_top) f[s] = v - ((int32_t)rank < r ? 1 : 0);
         }
         __syncthreads();
     }
@@ -527,17 +556,20 @@ __global__ void __launch_bounds__(kEncThreads) k_enc_chunks(EncArgs a) {
 __global__ void __launch_bounds__(512) k_enc_huff(EncArgs a) {
     constexpr uint32_t L = kHuffMaxLen;
     __shared__ uint64_t cnt[256];
+    __shared__ __align__(16) uint64_t key[256];  // count << 8 | byte for present bytes, else all ones
     __shared__ uint64_t leafw[256];   // present counts, ascending (bytes ascending on ties)
     __shared__ uint32_t leafsym[256];
     __shared__ uint64_t wbuf[2][512];  // item weights of a level and of the level below
     __shared__ uint8_t kind[L][512];   // 1: the item is a leaf
     __shared__ uint32_t mlev[L];       // leaves in each level's chosen prefix
     __shared__ uint32_t nlen[L + 1];   // codewords of each length
-    __shared__ uint32_t len[256];
+    __shared__ __align__(16) uint32_t len[256];
     __shared__ uint32_t npresent;
     const uint32_t t = threadIdx.x;
     if (t < 256) {
-        cnt[t] = at<uint64_t>(a.ws, a.w.counts)[t];
+        const uint64_t c = at<uint64_t>(a.ws, a.w.counts)[t];
+        cnt[t] = c;
+        key[t] = c ? (c << 8 | t) : ~0ull;
         len[t] = 0;
     }
     if (t <= L) nlen[t] = 0;
@@ -545,13 +577,17 @@ __global__ void __launch_bounds__(512) k_enc_huff(EncArgs a) {
     __syncthreads();
     if (t == 0) check_counts(a, cnt);
     if (t < 256 && cnt[t]) {
-        const uint64_t ct = cnt[t];
+        // rank by (count, byte): the keys below this byte's (16-byte reads,
+        // many in flight)
+        const uint64_t kt = key[t];
+        const ulonglong2 *k2 = reinterpret_cast<const ulonglong2 *>(key);
         uint32_t r = 0;
-        for (uint32_t u = 0; u < 256; ++u) {
-            const uint64_t cu = cnt[u];
-            r += (cu && (cu < ct || (cu == ct && u < t))) ? 1u : 0u;
+#pragma unroll 8
+        for (uint32_t q = 0; q < 128; ++q) {
+            const ulonglong2 w = k2[q];
+            r += (w.x < kt ? 1u : 0u) + (w.y < kt ? 1u : 0u);
         }
-        leafw[r] = ct;
+        leafw[r] = cnt[t];
         leafsym[r] = t;
         atomicAdd(&npresent, 1u);
     }
@@ -619,7 +655,14 @@ __global__ void __launch_bounds__(512) k_enc_huff(EncArgs a) {
                 uint32_t c = 0;
                 for (uint32_t j = 1; j < l; ++j) c = (c + nlen[j]) << 1;
                 uint32_t r = 0;
-                for (uint32_t u = 0; u < t; ++u) r += len[u] == l ? 1u : 0u;
+                const uint4 *l4 = reinterpret_cast<const uint4 *>(len);
+#pragma unroll 8
+                for (uint32_t q = 0; q < 64; ++q) {
+                    const uint4 w = l4[q];
+                    const uint32_t u = 4 * q;
+                    r += (u < t && w.x == l ? 1u : 0u) + (u + 1 < t && w.y == l ? 1u : 0u) +
+                         (u + 2 < t && w.z == l ? 1u : 0u) + (u + 3 < t && w.w == l ? 1u : 0u);
+                }
                 code = c + r;
             }
             hs[t] = l ? (__builtin_bitreverse32(code) >> (32u - l)) | (l << 16) : 0u;
