@@ -16,15 +16,19 @@
 //    interleaved rANS states, so a decode step is one instruction stream with
 //    no divergence;
 //  * a workgroup of 8 waves decodes 8 chunks of one tensor and shares one
-//    4096-entry slot table in LDS (4 bytes per entry: symbol byte, frequency,
-//    slot - cumulative frequency);
+//    4096-entry slot table in LDS (8 bytes per entry: frequency | symbol
+//    byte << 24, slot - cumulative frequency), built by a running maximum of
+//    the symbols' start marks;
 //  * renormalisation words are read in the container's order with a wave
 //    ballot of the lanes that need a word plus a masked popcount (mbcnt) of
 //    the lanes below, from a per-wave LDS ring that is refilled 1 KiB at a
 //    time with 16-byte coalesced loads;
 //  * after K steps each lane holds K consecutive outputs: the fp32 scale
 //    multiply, the RNE bf16 conversion (v_cvt_pk_bf16_f32) and one 16-byte
-//    store per lane (K = 8), i.e. a 1 KiB contiguous store per wave.
+//    non-temporal store per lane (K = 8), i.e. a 1 KiB contiguous store per
+//    wave; the fused GEMV variant dots them with x instead (v_dot2c).
+//  * Huffman-coded tensors (EntroLLM's codec) share everything but the table
+//    build and the step.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -348,18 +352,28 @@ __device__ __forceinline__ void build_lut_huff(const uint16_t *tab, uint32_t *lu
         }
     }
     __syncthreads();
+    // the per-length tables in registers (every slot tests the same ones;
+    // LDS reads in a dependent loop would serialise)
+    uint32_t fr[L + 1], cr[L + 1], orr[L + 1];
+#pragma unroll
+    for (uint32_t l = 1; l <= L; ++l) {
+        fr[l] = first[l];
+        cr[l] = cnt[l];
+        orr[l] = off[l];
+    }
     for (uint32_t v = tid; v < 4096u; v += kThreads) {
-        uint32_t e = L;  // fallback: 12 bits, symbol 0
         const uint32_t rv = __builtin_bitreverse32(v);
-        for (uint32_t l = 1; l <= L; ++l) {
-            const uint32_t code = rv >> (32u - l);  // the low l bits of v, first bit highest
-            const uint32_t i = code - first[l];
-            if (i < cnt[l]) {
-                e = l | (sorted[off[l] + i] << 24);
-                break;
+        // the shortest length whose code range holds the low bits of v
+        uint32_t len = L, idx = 0xFFFFFFFFu;  // fallback: 12 bits, symbol 0
+#pragma unroll
+        for (uint32_t l = L; l >= 1; --l) {
+            const uint32_t i = (rv >> (32u - l)) - fr[l];  // the low l bits of v, first bit highest
+            if (i < cr[l]) {
+                len = l;
+                idx = orr[l] + i;
             }
         }
-        lut[v] = e;
+        lut[v] = len | ((idx != 0xFFFFFFFFu ? sorted[idx] : 0u) << 24);
     }
     __syncthreads();
 }
