@@ -187,11 +187,11 @@ def cpu_baseline(conts, target_s: float = 10.0):
     threads = host_cores()
     outs = [np.zeros(int(c.hdr.n), np.uint16) for c in conts]
 
-    def run(per_tensor):
+    def run(per_tensor, nthreads=threads):
         t0 = time.perf_counter()
         n = 0
         for c, k, o in zip(conts, per_tensor, outs):
-            flags = oracle.decode_chunks(c.host, 0, k, threads, bf16_out=o)
+            flags = oracle.decode_chunks(c.host, 0, k, nthreads, bf16_out=o)
             if flags:
                 raise RuntimeError(f"oracle decode flags {flags}")
             n += min(int(c.hdr.n), k * int(c.hdr.chunk_symbols))
@@ -212,11 +212,24 @@ def cpu_baseline(conts, target_s: float = 10.0):
             total_n += m
         dt, n = total_t, total_n
     whole = all(k == int(c.hdr.n_chunks) for c, k in zip(conts, ks))
-    what = "the whole 7-tensor block" if whole else f"chunks [0, k) of each tensor, k = {ks}"
+    what = (f"the whole {len(conts)}-tensor block" if len(conts) > 1 else "the whole tensor") if whole \
+        else f"chunks [0, k) of each tensor, k = {ks}"
     desc = (f"{what} ({n // reps / 1e6:.1f} M weights per pass, {reps} pass(es)), decoded + "
             f"dequantised to bf16 by the oracle with {threads} threads")
+    # the same oracle on one thread: one chunk of each tensor, repeated to ~2 s
+    one = [1 for _ in conts]
+    d1, n1 = run(one, 1)
+    r1 = max(1, int(2.0 / max(d1, 1e-3)))
+    t1, m1 = 0.0, 0
+    for _ in range(r1):
+        d, m = run(one, 1)
+        t1 += d
+        m1 += m
     return {"value": round(2.0 * n / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": desc, "seconds": round(dt, 2)}
+            "sample": desc, "seconds": round(dt, 2),
+            "single_thread": {"value": round(2.0 * m1 / t1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                              "sample": f"chunk 0 of each of the {len(conts)} tensor(s), {r1} pass(es)",
+                              "seconds": round(t1, 2)}}
 
 
 def copy_ceiling(nbytes: int) -> float:
