@@ -33,6 +33,7 @@
 //           inside the scratch is wave-uniform, so each lane realigns two
 //           aligned loads), escape list, zero gaps
 #include <hip/hip_runtime.h>
+#include <type_traits>
 
 #include <cstdint>
 
@@ -687,12 +688,15 @@ constexpr uint32_t kWordRow = 33;    // u16 per lane row of the 32-word stream r
 // step, into a 32-word LDS ring; the word a lane takes is always complete
 // by then: when it needs one it holds < 12 bits, so the 16 bits it takes
 // end within its next 28 codewords (each at least one bit), and a lane's
-// unused packed bits stay below 28 * 12 + 16. At the stream's end the
-// partial last word is packed zero-padded, and a lane asking for more gets
-// zero words. The symbols' (reversed codeword, length) entries of the next
-// steps are staged in a per-lane 64-step LDS ring, their bytes loaded about
-// 32 steps before they are staged. Words leave through the LDS output ring
-// as in the rANS encoder, filled from the chunk's start.
+// unused packed bits stay below 28 * 12 + 16. The (reversed codeword,
+// length) entries of the next steps are staged in a per-lane 64-step LDS
+// ring, their bytes loaded about 32 steps before they are staged; a step
+// past the lane's last symbol stages the empty entry (no bits), so the
+// steps need no lane mask. At its end step the lane's pack writes the
+// zero-padded partial word and one zero word after it: a lane asks for at
+// most one word past its stream (after it, it holds >= 16 bits more than it
+// will consume). Words leave through the LDS output ring as in the rANS
+// encoder, filled from the chunk's start.
 template <int K>
 __global__ void __launch_bounds__(kEncThreads) k_enc_hchunks(EncArgs a) {
     __shared__ uint32_t hs[257];
@@ -722,47 +726,56 @@ __global__ void __launch_bounds__(kEncThreads) k_enc_hchunks(EncArgs a) {
         constexpr uint32_t P = K >= 8 ? 4u : 32u / K;
         static_assert((DELTA + 1) * K <= 64, "entry ring");
         const uint32_t groups = (nk + G - 1) / G;
-        const uint32_t T = groups * K;
-        auto pos = [&](uint32_t st) { return (st / K) * G + lane * K + (st % K); };
-        // entries: reversed codeword | length << 12
+        const uint32_t full = nk / G;          // groups with every lane's run inside the chunk
+        const uint32_t tail = nk - full * G;   // symbols of the partial group
+        // this lane's symbols in the partial group; the step its stream ends
+        const uint32_t mine = tail > lane * K ? (tail - lane * K < (uint32_t)K ? tail - lane * K : (uint32_t)K) : 0u;
+        const uint32_t endst = full * K + mine;
+        // entries: reversed codeword | length << 12; the empty entry past the lane's symbols
         auto stage_group = [&](uint32_t g, const uint32_t (&w)[W]) {
-            if (g >= groups) return;
 #pragma unroll
             for (int i = 0; i < K; ++i) {
                 const uint32_t e = hs[(w[i / 4] >> (8 * (i % 4))) & 0xFFu];
-                er[(g * K + i) & 63u] = (uint16_t)((e & 0xFFFu) | ((e >> 16) << 12));
+                const uint16_t v = (uint16_t)((e & 0xFFFu) | ((e >> 16) << 12));
+                er[(g * K + i) & 63u] = g < full || (g == full && (uint32_t)i < mine) ? v : (uint16_t)0;
             }
         };
-        uint32_t acc = 0, ab = 0;      // packed bits not yet in a word, their count
-        uint32_t wprod = 0, wnext = 0; // words packed; the next one to hand out
-        bool ended = false;            // the stream is fully packed
-        // branch-free: past the stream's end the entry reads as 0 bits, and
-        // the first such step flushes the partial word
+        uint32_t acc = 0, ab = 0;  // packed bits not yet in a word, their count
+        uint32_t wprod = 0;        // words packed
         auto pack = [&](uint32_t st) {
-            const bool valid = st < T && pos(st) < nk;
-            const uint32_t e0 = er[st & 63u];
-            const uint32_t e = valid ? e0 : 0u;
+            const uint32_t e = er[st & 63u];
             acc |= (e & 0xFFFu) << ab;
             ab += e >> 12;
-            const bool emit = ab >= 16 || (!valid && !ended && ab != 0);
-            if (emit) wr[wprod & 31u] = (uint16_t)acc;
-            wprod += emit ? 1u : 0u;
-            acc = emit ? acc >> 16 : acc;
-            ab = emit ? (ab >= 16 ? ab - 16 : 0u) : ab;
-            ended = ended || !valid;
+            if (ab >= 16u) {
+                wr[wprod & 31u] = (uint16_t)acc;
+                ++wprod;
+                acc >>= 16;
+                ab -= 16u;
+            }
+            if (st == endst) {
+                // the stream ended before this step (whose entry is empty)
+                if (ab != 0u) {
+                    wr[wprod & 31u] = (uint16_t)acc;
+                    ++wprod;
+                }
+                wr[wprod & 31u] = 0;
+                acc = 0;
+                ab = 0;
+            }
         };
         // the first DELTA groups staged directly, the next P in flight
-        for (uint32_t g = 0; g < DELTA && g < groups; ++g) {
+        for (uint32_t g = 0; g < DELTA; ++g) {
             uint32_t w[W];
             load_run<K>(sym, g * G + lane * K, nk, w);
             stage_group(g, w);
         }
-        uint32_t q[P][W];
+        uint32_t q[P][W] = {};
 #pragma unroll
         for (uint32_t d = 0; d < P; ++d)
             if (DELTA + d < groups) load_run<K>(sym, (DELTA + d) * G + lane * K, nk, q[d]);
         for (uint32_t st = 0; st < kHuffAhead; ++st) pack(st);
         uint32_t held = 0;                    // the decoder's bits at this step
+        uint32_t wnext = 0;                   // this lane's next word to hand out
         uint32_t ptr = 0, flushed = 0;        // words written; words already in the scratch
         for (uint32_t g0 = 0; g0 < groups; g0 += P) {
 #pragma unroll
@@ -772,22 +785,32 @@ __global__ void __launch_bounds__(kEncThreads) k_enc_hchunks(EncArgs a) {
                 // q[d] holds group g + DELTA: stage it, then load group g + DELTA + P
                 stage_group(g + DELTA, q[d]);
                 if (g + DELTA + P < groups) load_run<K>(sym, (g + DELTA + P) * G + lane * K, nk, q[d]);
+                // the group's steps; lanes past the chunk (partial group only) take no words
+                auto steps = [&](auto part) {
 #pragma unroll
-                for (uint32_t i = 0; i < K; ++i) {
-                    const uint32_t t = g * K + i;
-                    pack(t + kHuffAhead);
-                    const bool active = pos(t) < nk;
-                    const bool need = active && held < 12;
-                    const uint64_t m = __builtin_amdgcn_ballot_w64(need);
-                    const uint32_t slot = __builtin_amdgcn_mbcnt_hi(
-                        (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, ptr));
-                    const uint16_t w0 = wr[wnext & 31u];
-                    const uint32_t len = er[t & 63u] >> 12;
-                    if (need) ring[slot & (kEncRing - 1u)] = wnext < wprod ? w0 : (uint16_t)0;
-                    wnext += need ? 1u : 0u;
-                    held = held + (need ? 16u : 0u) - (active ? len : 0u);
-                    ptr += (uint32_t)__builtin_popcountll(m);
-                }
+                    for (uint32_t i = 0; i < K; ++i) {
+                        const uint32_t t = g * K + i;
+                        // read before this step's packing: a word the lane takes
+                        // now was complete 28 steps ahead, as was the zero word
+                        // after its stream (the stream ends within 12 steps then)
+                        const uint16_t w = wr[wnext & 31u];
+                        const uint32_t len = (uint32_t)er[t & 63u] >> 12;
+                        pack(t + kHuffAhead);
+                        const bool need = decltype(part)::value ? held < 12u && t < endst : held < 12u;
+                        const uint64_t m = __builtin_amdgcn_ballot_w64(need);
+                        if (need) {
+                            const uint32_t slot = __builtin_amdgcn_mbcnt_hi(
+                                (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, ptr));
+                            ring[slot & (kEncRing - 1u)] = w;
+                            ++wnext;
+                            held += 16u;
+                        }
+                        held -= len;
+                        ptr += (uint32_t)__builtin_popcountll(m);
+                    }
+                };
+                if (g < full) steps(std::false_type{});
+                else steps(std::true_type{});
                 while (ptr >= flushed + kEncFlush) {
                     const uint32_t b = flushed + lane * 8u;
                     *reinterpret_cast<uint4 *>(scr + b) =
