@@ -676,9 +676,36 @@ __global__ void __launch_bounds__(512) k_enc_huff(EncArgs a) {
     if (t == 0) write_header(a);
 }
 
-constexpr uint32_t kHuffAhead = 28;  // steps a lane's stream is packed ahead of the decoder replay
-constexpr uint32_t kEntRow = 66;     // u16 per lane row of the 64-step entry ring (+2: fewer bank conflicts)
-constexpr uint32_t kWordRow = 33;    // u16 per lane row of the 32-word stream ring
+constexpr uint32_t kHuffAhead = 28;   // steps a lane's stream is packed ahead of the decoder replay
+constexpr uint32_t kWordRow = 33;     // u16 per lane row of the 32-word stream ring
+constexpr uint32_t kHuffRing = 1024;  // words of a wave's output ring (flushed every 8 steps)
+constexpr uint32_t kHuffBlk = 32;     // steps per unrolled block: the lane's bytes of a block in 8 dwords
+
+// This lane's 32 bytes of the steps [32 b, 32 b + 32), in step order (its
+// K-runs of the block's 32 / K groups); positions past the chunk read as 0.
+template <int K>
+__device__ __forceinline__ void load_block(const uint8_t *sym, uint32_t b, uint32_t lane, uint32_t nk,
+                                           uint32_t (&v)[8]) {
+    constexpr uint32_t G = 64u * K;
+    constexpr int W = (K + 3) / 4;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0;
+#pragma unroll
+    for (uint32_t r = 0; r < kHuffBlk / K; ++r) {
+        uint32_t w[W];
+        load_run<K>(sym, (b * (kHuffBlk / K) + r) * G + lane * K, nk, w);
+        if constexpr (K >= 4) {
+#pragma unroll
+            for (int j = 0; j < W; ++j) v[r * K / 4 + j] = w[j];
+        } else {
+            v[r * K / 4] |= w[0] << (8 * ((r * K) % 4));
+        }
+    }
+}
+
+__device__ __forceinline__ uint32_t byte_of(const uint32_t (&v)[8], uint32_t j) {
+    return (v[j / 4] >> (8 * (j % 4))) & 0xFFu;
+}
 
 // One wave per chunk, steps walked forwards, replaying the decoder: at each
 // step a lane holding (decoder side) fewer than 12 bits takes its next
@@ -688,21 +715,21 @@ constexpr uint32_t kWordRow = 33;    // u16 per lane row of the 32-word stream r
 // step, into a 32-word LDS ring; the word a lane takes is always complete
 // by then: when it needs one it holds < 12 bits, so the 16 bits it takes
 // end within its next 28 codewords (each at least one bit), and a lane's
-// unused packed bits stay below 28 * 12 + 16. The (reversed codeword,
-// length) entries of the next steps are staged in a per-lane 64-step LDS
-// ring, their bytes loaded about 32 steps before they are staged; a step
-// past the lane's last symbol stages the empty entry (no bits), so the
-// steps need no lane mask. At its end step the lane's pack writes the
-// zero-padded partial word and one zero word after it: a lane asks for at
-// most one word past its stream (after it, it holds >= 16 bits more than it
-// will consume). Words leave through the LDS output ring as in the rANS
-// encoder, filled from the chunk's start.
+// unused packed bits stay below 28 * 12 + 16. The lane's symbol bytes stay
+// in registers, 32 steps to a block (the block being replayed, the next
+// one, which the packing reaches into, and one in flight), and both walks
+// look their (reversed codeword, length) up in the LDS code table; a step
+// past the lane's last symbol looks up the empty entry (table index 256,
+// which holds 0), so no step needs a lane mask. At its end step the lane's
+// pack writes the zero-padded partial word and one zero word after it: a
+// lane asks for at most one word past its stream (after it, it holds >= 16
+// bits more than it will consume). Words leave through a 1,024-word LDS
+// output ring, 512 at a time, checked every 8 steps (a step adds at most 64).
 template <int K>
 __global__ void __launch_bounds__(kEncThreads) k_enc_hchunks(EncArgs a) {
     __shared__ uint32_t hs[257];
-    __shared__ __align__(16) uint16_t entring[kEncWaves][64 * kEntRow];
     __shared__ __align__(16) uint16_t wordring[kEncWaves][64 * kWordRow];
-    __shared__ __align__(16) uint16_t rings[kEncWaves][kEncRing];
+    __shared__ __align__(16) uint16_t rings[kEncWaves][kHuffRing];
     for (uint32_t i = threadIdx.x; i < 257; i += blockDim.x) hs[i] = at<uint32_t>(a.ws, a.w.table)[i];
     __syncthreads();
     const uint32_t lane = threadIdx.x & 63u;
@@ -716,36 +743,27 @@ __global__ void __launch_bounds__(kEncThreads) k_enc_hchunks(EncArgs a) {
         const uint8_t *sym = a.sym + p0;
         uint16_t *scr = at<uint16_t>(a.ws, a.w.scratch) + p0;
         uint16_t *ring = rings[wave];
-        uint16_t *er = &entring[wave][lane * kEntRow];
         uint16_t *wr = &wordring[wave][lane * kWordRow];
         constexpr uint32_t G = 64u * K;
-        constexpr int W = (K + 3) / 4;
-        // groups staged ahead of the one being replayed (at least 28 steps),
-        // and loads in flight (about 32 steps ahead of their staging)
-        constexpr uint32_t DELTA = (kHuffAhead + K - 1) / K;
-        constexpr uint32_t P = K >= 8 ? 4u : 32u / K;
-        static_assert((DELTA + 1) * K <= 64, "entry ring");
         const uint32_t groups = (nk + G - 1) / G;
         const uint32_t full = nk / G;          // groups with every lane's run inside the chunk
         const uint32_t tail = nk - full * G;   // symbols of the partial group
         // this lane's symbols in the partial group; the step its stream ends
         const uint32_t mine = tail > lane * K ? (tail - lane * K < (uint32_t)K ? tail - lane * K : (uint32_t)K) : 0u;
         const uint32_t endst = full * K + mine;
-        // entries: reversed codeword | length << 12; the empty entry past the lane's symbols
-        auto stage_group = [&](uint32_t g, const uint32_t (&w)[W]) {
-#pragma unroll
-            for (int i = 0; i < K; ++i) {
-                const uint32_t e = hs[(w[i / 4] >> (8 * (i % 4))) & 0xFFu];
-                const uint16_t v = (uint16_t)((e & 0xFFFu) | ((e >> 16) << 12));
-                er[(g * K + i) & 63u] = g < full || (g == full && (uint32_t)i < mine) ? v : (uint16_t)0;
-            }
+        const uint32_t nblk = (groups * K + kHuffBlk - 1) / kHuffBlk;  // steps past the chunk do nothing
+        const uint32_t all_in = full * K;      // steps below it lie in every lane's stream
+        // (reversed codeword | length << 16) of step st's byte; CHECK: the
+        // empty entry from the lane's end step on
+        auto entry = [&](uint32_t byte, uint32_t st, auto check) -> uint32_t {
+            if constexpr (decltype(check)::value) return hs[st < endst ? byte : 256u];
+            else return hs[byte];
         };
         uint32_t acc = 0, ab = 0;  // packed bits not yet in a word, their count
         uint32_t wprod = 0;        // words packed
-        auto pack = [&](uint32_t st) {
-            const uint32_t e = er[st & 63u];
+        auto pack = [&](uint32_t e, uint32_t st) {
             acc |= (e & 0xFFFu) << ab;
-            ab += e >> 12;
+            ab += e >> 16;
             if (ab >= 16u) {
                 wr[wprod & 31u] = (uint16_t)acc;
                 ++wprod;
@@ -763,65 +781,65 @@ __global__ void __launch_bounds__(kEncThreads) k_enc_hchunks(EncArgs a) {
                 ab = 0;
             }
         };
-        // the first DELTA groups staged directly, the next P in flight
-        for (uint32_t g = 0; g < DELTA; ++g) {
-            uint32_t w[W];
-            load_run<K>(sym, g * G + lane * K, nk, w);
-            stage_group(g, w);
-        }
-        uint32_t q[P][W] = {};
+        uint32_t cur[8], nxt[8], pre[8];
+        load_block<K>(sym, 0, lane, nk, cur);
+        load_block<K>(sym, 1, lane, nk, nxt);
+        load_block<K>(sym, 2, lane, nk, pre);
 #pragma unroll
-        for (uint32_t d = 0; d < P; ++d)
-            if (DELTA + d < groups) load_run<K>(sym, (DELTA + d) * G + lane * K, nk, q[d]);
-        for (uint32_t st = 0; st < kHuffAhead; ++st) pack(st);
+        for (uint32_t st = 0; st < kHuffAhead; ++st) pack(entry(byte_of(cur, st), st, std::true_type{}), st);
         uint32_t held = 0;                    // the decoder's bits at this step
         uint32_t wnext = 0;                   // this lane's next word to hand out
         uint32_t ptr = 0, flushed = 0;        // words written; words already in the scratch
-        for (uint32_t g0 = 0; g0 < groups; g0 += P) {
+        for (uint32_t bk = 0; bk < nblk; ++bk) {
+            auto body = [&](auto check) {
+                constexpr bool C = decltype(check)::value;
 #pragma unroll
-            for (uint32_t d = 0; d < P; ++d) {
-                const uint32_t g = g0 + d;
-                if (g >= groups) continue;  // (the rest of this batch is past the chunk)
-                // q[d] holds group g + DELTA: stage it, then load group g + DELTA + P
-                stage_group(g + DELTA, q[d]);
-                if (g + DELTA + P < groups) load_run<K>(sym, (g + DELTA + P) * G + lane * K, nk, q[d]);
-                // the group's steps; lanes past the chunk (partial group only) take no words
-                auto steps = [&](auto part) {
-#pragma unroll
-                    for (uint32_t i = 0; i < K; ++i) {
-                        const uint32_t t = g * K + i;
-                        // read before this step's packing: a word the lane takes
-                        // now was complete 28 steps ahead, as was the zero word
-                        // after its stream (the stream ends within 12 steps then)
-                        const uint16_t w = wr[wnext & 31u];
-                        const uint32_t len = (uint32_t)er[t & 63u] >> 12;
-                        pack(t + kHuffAhead);
-                        const bool need = decltype(part)::value ? held < 12u && t < endst : held < 12u;
-                        const uint64_t m = __builtin_amdgcn_ballot_w64(need);
-                        if (need) {
-                            const uint32_t slot = __builtin_amdgcn_mbcnt_hi(
-                                (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, ptr));
-                            ring[slot & (kEncRing - 1u)] = w;
-                            ++wnext;
-                            held += 16u;
-                        }
-                        held -= len;
-                        ptr += (uint32_t)__builtin_popcountll(m);
+                for (uint32_t j = 0; j < kHuffBlk; ++j) {
+                    const uint32_t t = bk * kHuffBlk + j;
+                    // read before this step's packing: a word the lane takes
+                    // now was complete 28 steps ahead, as was the zero word
+                    // after its stream (the stream ends within 12 steps then)
+                    const uint16_t w = wr[wnext & 31u];
+                    const uint32_t len = entry(byte_of(cur, j), t, check) >> 16;
+                    const uint32_t jp = j + kHuffAhead;
+                    uint32_t bp;
+                    if (jp < kHuffBlk) bp = byte_of(cur, jp);
+                    else bp = byte_of(nxt, jp - kHuffBlk);
+                    pack(entry(bp, t + kHuffAhead, check), t + kHuffAhead);
+                    const bool need = C ? held < 12u && t < endst : held < 12u;
+                    const uint64_t m = __builtin_amdgcn_ballot_w64(need);
+                    if (need) {
+                        const uint32_t slot = __builtin_amdgcn_mbcnt_hi(
+                            (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, ptr));
+                        ring[slot & (kHuffRing - 1u)] = w;
+                        ++wnext;
+                        held += 16u;
                     }
-                };
-                if (g < full) steps(std::false_type{});
-                else steps(std::true_type{});
-                while (ptr >= flushed + kEncFlush) {
-                    const uint32_t b = flushed + lane * 8u;
-                    *reinterpret_cast<uint4 *>(scr + b) =
-                        *reinterpret_cast<const uint4 *>(ring + (b & (kEncRing - 1u)));
-                    flushed += kEncFlush;
+                    held -= len;
+                    ptr += (uint32_t)__builtin_popcountll(m);
+                    if (j % 8u == 7u) {
+                        while (ptr >= flushed + kEncFlush) {
+                            const uint32_t b = flushed + lane * 8u;
+                            *reinterpret_cast<uint4 *>(scr + b) =
+                                *reinterpret_cast<const uint4 *>(ring + (b & (kHuffRing - 1u)));
+                            flushed += kEncFlush;
+                        }
+                    }
                 }
+            };
+            // every step of this block and of the next (which the packing reaches) inside every lane's stream
+            if ((bk + 2u) * kHuffBlk <= all_in) body(std::false_type{});
+            else body(std::true_type{});
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                cur[i] = nxt[i];
+                nxt[i] = pre[i];
             }
+            if (bk + 3u < nblk) load_block<K>(sym, bk + 3u, lane, nk, pre);
         }
         // the last words (the rest of their 8-word block is scratch nobody reads)
         const uint32_t b = flushed + lane * 8u;
-        if (b < ptr) *reinterpret_cast<uint4 *>(scr + b) = *reinterpret_cast<const uint4 *>(ring + (b & (kEncRing - 1u)));
+        if (b < ptr) *reinterpret_cast<uint4 *>(scr + b) = *reinterpret_cast<const uint4 *>(ring + (b & (kHuffRing - 1u)));
         words = ptr;
     }
     if (lane == 0) {
