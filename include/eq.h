@@ -104,7 +104,7 @@ typedef int32_t eq_status;
 #define EQ_ERANGE (-2)       /* output buffer too small; *out_len holds the size */
 #define EQ_ECORRUPT (-3)     /* container header or tables inconsistent */
 #define EQ_EHIP (-4)         /* HIP launch / runtime error */
-#define EQ_EUNSUPPORTED (-5) /* valid container this build cannot decode */
+#define EQ_EUNSUPPORTED (-5) /* valid container this library version cannot decode */
 #define EQ_ENOMEM (-6)       /* host allocation failed (encoder scratch) */
 
 /* Device status bits (ORed into eq_block.d_status). */
