@@ -173,6 +173,31 @@ def test_huffman_random_layouts_and_one_symbol():
                     codec=eq.EQ_CODEC_HUFFMAN)
 
 
+def test_huffman_length_limited_codes_ragged_chunks():
+    """Sixteen bytes with Fibonacci counts: an unlimited Huffman code would be
+    15 deep, so the 12-bit limit binds and some codewords are 12 bits long;
+    ragged chunk and lane ends for every lane run."""
+    rng = np.random.default_rng(47)
+    fib = [1, 1]
+    while len(fib) < 16:
+        fib.append(fib[-1] + fib[-2])
+    present = rng.choice(256, size=16, replace=False).astype(np.uint8)
+    base = np.repeat(present, fib)
+    for K in (1, 2, 4, 8, 16):
+        Z = 64 * K * 4
+        n = 3 * base.size + 64 * K + 37
+        sym = np.concatenate([rng.permutation(base) for _ in range(4)])[:n]
+        scales = rng.uniform(0.5, 2.0, 1).astype(np.float32)
+        log(f"case device Huffman encode 12-bit codes K={K} n={n}")
+        c = check_equal(sym, scales, 1, 1, n, Z, K, what=f"huffman 12-bit K={K}", codec=eq.EQ_CODEC_HUFFMAN)
+        h = eq.eq_parse_header(c)
+        lens = np.frombuffer(c[h.off_freq:h.off_freq + 512].tobytes(), np.uint16)
+        assert lens.max() == 12 and np.count_nonzero(lens == 12) >= 2, lens[lens > 0]
+        got, st = run_u8([eq.DeviceContainer(c, device="cuda")], n)
+        assert st == 0
+        assert_same(got, sym, f"round trip K={K}")
+
+
 def test_adaptive_tables_random_layouts():
     rng = np.random.default_rng(43)
     for it in range(40):
