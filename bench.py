@@ -109,29 +109,34 @@ def counter_record(name: str, key: str, kernel_src: str):
 
 
 def build_block(cfg: int, layer: int = 0, lane_run: int = 8, use_cache: bool = True,
-                tensors=None, whole_rows: bool = False, codec: int = 0):
+                tensors=None, whole_rows: bool = False, codec: int = 0, bits: float | None = None):
     """Encode one block with the library's host encoder and place its
     containers in device memory (all tensors, or the listed indices). Chunks
     are 64 Ki symbols, or with whole_rows the nearest multiple of the row
     length (what the fused decode + GEMV needs). codec 0 = rANS, 1 = Huffman.
     With EQ_BENCH_CACHE=<dir> the encoded containers are kept there as .npy
-    files and reused."""
+    files and reused. bits: another entropy for the synthetic codes (bits
+    per weight) than the configuration's."""
+    import dataclasses
     import numpy as np
     import synth
     from rans_decode_amd import eq
     specs = synth.config_specs(cfg)
+    if bits is not None:
+        specs = [dataclasses.replace(sp, bits=bits) for sp in specs]
     cache = os.environ.get("EQ_BENCH_CACHE") if use_cache else None
     conts = []
     for i, sp in enumerate(specs):
         if tensors is not None and i not in tensors:
             continue
         Z = whole_row_chunk(sp.cols, lane_run) if whole_rows else synth.CHUNK_SYMBOLS
-        path = (os.path.join(cache, f"cfg{cfg}_layer{layer}_t{i}_k{lane_run}_z{Z}_c{codec}.npy")
+        btag = "" if bits is None else f"_b{bits:g}"
+        path = (os.path.join(cache, f"cfg{cfg}_layer{layer}_t{i}_k{lane_run}_z{Z}_c{codec}{btag}.npy")
                 if cache else None)
         if path and os.path.exists(path):
             blob = np.load(path)
         else:
-            t = synth.make_tensor(cfg, layer, i)
+            t = synth.make_tensor(cfg, layer, i, spec=sp)
             tab = eq.build_tables(t.symbols)
             esc = t.esc_idx.size > 0
             blob = eq.encode_host(tab, sp.dtype, sp.rows, sp.cols, t.symbols, t.scales,
@@ -273,7 +278,7 @@ def bench_block(args):
     cfg, what = WORKLOADS[args.workload]
     codec = CODECS[args.codec]
     t0 = time.perf_counter()
-    specs, conts = build_block(cfg, 0, args.lane_run, codec=codec)
+    specs, conts = build_block(cfg, 0, args.lane_run, codec=codec, bits=args.bits)
     offs = synth.block_offsets(specs)
     n = offs[-1]
     log(f"block built in {time.perf_counter() - t0:.1f} s: {n} weights, "
@@ -314,7 +319,7 @@ def bench_block(args):
     algo = comp + outb
     achieved = algo / (avg_ms * 1e-3) / 1e9
     traffic = (traffic_record(os.path.join(ROOT, "rans_decode_amd", "csrc", "decode.hip"))
-               if cfg == 4 and codec == 0 else None)
+               if cfg == 4 and codec == 0 and args.bits is None else None)
     total_container = sum(c.nbytes for c in conts)
     rec = {
         "metric": "decoded weight GB/s (bf16 out) and % HBM roofline, 70B-shaped block decode"
@@ -331,7 +336,8 @@ def bench_block(args):
         "dtype": "u32/f32",
         "data": "synthetic",
         "config": {
-            "workload": f"{what}; {args.codec} codec, 64Ki-symbol chunks, 64 lanes, K={args.lane_run}, bf16 out",
+            "workload": f"{what}; {args.codec} codec, 64Ki-symbol chunks, 64 lanes, K={args.lane_run}, bf16 out"
+                        + ("" if args.bits is None else f"; codes drawn at {args.bits:g} bits per weight"),
             "codec": args.codec,
             "weights": n,
             "container_bytes": total_container,
@@ -849,6 +855,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-ceiling", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--bits", type=float, default=None,
+                    help="block workloads: entropy of the synthetic codes in bits per weight "
+                         "(default: the configuration's)")
     ap.add_argument("--layers", type=int, default=80, help="blocks in the model80 workload")
     ap.add_argument("--codec", choices=sorted(CODECS), default="rans",
                     help="entropy coder of the block workloads' containers (rANS: EntQuant's ANS; "
