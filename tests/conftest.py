@@ -63,3 +63,40 @@ def gpu_available():
         return torch.cuda.is_available()
     except Exception:
         return False
+
+
+@pytest.fixture
+def planted(tmp_path):
+    """planted(old, new): a copy of the oracle's C source with one planted
+    mistake (old -> new, on the CPU), built and swapped in for the oracle
+    package's calls until the test ends."""
+    import contextlib
+
+    import oracle
+
+    src_path = os.path.join(ROOT, "oracle", "eq_oracle.c")
+    made = []
+
+    def build(old, new):
+        src = open(src_path).read()
+        assert src.count(old) == 1, f"mutation target not unique: {old!r}"
+        p = tmp_path / f"planted{len(made)}.c"
+        p.write_text(src.replace(old, new))
+        so = str(tmp_path / f"libplanted{len(made)}.so")
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-shared", "-fPIC", "-ffp-contract=off", str(p),
+                               "-o", so, "-lpthread"])
+        made.append(so)
+
+        @contextlib.contextmanager
+        def use():
+            saved = oracle.LIB_PATH
+            oracle.LIB_PATH = so
+            oracle.lib.cache_clear()
+            try:
+                yield oracle
+            finally:
+                oracle.LIB_PATH = saved
+                oracle.lib.cache_clear()
+        return use()
+
+    return build

@@ -45,25 +45,29 @@ def test_smoke_int8_escapes():
 @pytest.mark.parametrize("cfg", [1, 2])
 def test_config_single_matrix(cfg):
     t = synth.make_tensor(cfg, 0, 0)
-    log(f"case config {cfg}: {t.spec}")
-    _check_tensor(t, what=f"config {cfg}")
+    Z = synth.config_chunk(cfg)
+    log(f"case config {cfg}: {t.spec}, {Z}-symbol chunks")
+    _check_tensor(t, Z, what=f"config {cfg}")
+    if Z != 65536:
+        _check_tensor(t, 65536, what=f"config {cfg}, 64 Ki chunks")
 
 
-def _block_case(cfg, layer=0):
+def _block_case(cfg, layer=0, chunk=None):
     specs = synth.config_specs(cfg)
     offs = synth.block_offsets(specs)
     tensors = [synth.make_tensor(cfg, layer, i) for i in range(len(specs))]
-    blobs = [encode(t) for t in tensors]
+    blobs = [encode(t, chunk or synth.config_chunk(cfg)) for t in tensors]
     return specs, offs, tensors, blobs
 
 
-@pytest.mark.parametrize("cfg", [3, 4])
-def test_config_block_full(cfg):
+@pytest.mark.parametrize("cfg,chunk", [(3, None), (4, None), (3, 65536), (4, 65536)])
+def test_config_block_full(cfg, chunk):
     """The whole block into one buffer, one call (config 3: 7B E4M3 block,
     202 M weights; config 4: 70B int8 block with escapes, 856 M weights),
-    every output element compared."""
-    log(f"case config {cfg} block: generating")
-    specs, offs, tensors, blobs = _block_case(cfg)
+    every output element compared; at the configuration's chunk size and at
+    64 Ki."""
+    log(f"case config {cfg} block, chunk {chunk or synth.config_chunk(cfg)}: generating")
+    specs, offs, tensors, blobs = _block_case(cfg, chunk=chunk)
     conts = [_dev(b) for b in blobs]
     log(f"case config {cfg} block: decode")
     got, st = run_bf16(conts, offs[-1], offsets=offs[:-1])

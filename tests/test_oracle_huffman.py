@@ -159,6 +159,64 @@ def test_golden_one_lane_container():
     assert fl == 0 and np.array_equal(d, msg)
 
 
+def _w7_case():
+    g = {k: v[0] for k, v in read_golden("w7_huffman_two_lanes.txt").items()}
+    t = np.zeros(256, np.uint16)
+    for kv in g["lengths"].split():
+        sy, ln = kv.split(":")
+        t[int(sy)] = int(ln)
+    msg = np.array([int(x) for x in g["message"].split()], np.uint8)
+    return g, t, msg
+
+
+def _w7_mismatches(orc, g, t, msg):
+    blob = orc.encode(1, 1, msg.size, msg, np.ones(1, np.float32), t, int(g["chunk_symbols"]),
+                      int(g["lane_run"]), codec=orc.CODEC_HUFF)
+    h = orc.header(blob)
+    bad = []
+    if int(blob[h["off_dir"] + 8:h["off_dir"] + 12].view(np.uint32)[0]) != int(g["word_count"]):
+        bad.append("word count")
+    exp = [int(w, 16) for w in g["words_padded"].split()]
+    if blob[h["off_words"]:h["off_words"] + 2 * len(exp)].view(np.uint16).tolist() != exp:
+        bad.append("words")
+    d, fl = orc.decode_symbols(blob)
+    if fl or not np.array_equal(d, msg):
+        bad.append("decode")
+    return bad, blob
+
+
+def test_golden_two_lane_container():
+    """Two Huffman lanes take words in the same steps (ascending lanes), lane
+    1's bitstream packed like lane 0's."""
+    g, t, msg = _w7_case()
+    bad, _ = _w7_mismatches(oracle, g, t, msg)
+    assert bad == []
+
+
+def test_two_lane_golden_catches_planted_mistakes(planted):
+    g, t, msg = _w7_case()
+    # the encoder's replay of the refills serves the lanes in descending order
+    old = ("        for (uint32_t j = 0; j < OR_LANES; j++) {\n"
+           "            if (lane_pos(t, j, K) >= nk || have[j] >= 12) continue;")
+    new = ("        for (uint32_t j = OR_LANES; j-- > 0;) {\n"
+           "            if (lane_pos(t, j, K) >= nk || have[j] >= 12) continue;")
+    with planted(old, new) as orc:
+        assert _w7_mismatches(orc, g, t, msg)[0] != []
+    # the decoder refills in descending lane order: it misreads the good container
+    _, blob = _w7_mismatches(oracle, g, t, msg)
+    old = ("        for (uint32_t j = 0; j < OR_LANES; j++) {\n"
+           "            if (lane_pos(t, j, K) >= nk || n[j] >= 12) continue;")
+    new = ("        for (uint32_t j = OR_LANES; j-- > 0;) {\n"
+           "            if (lane_pos(t, j, K) >= nk || n[j] >= 12) continue;")
+    with planted(old, new) as orc:
+        d, fl = orc.decode_symbols(blob)
+        assert fl != 0 or not np.array_equal(d, msg)
+    # a lane refills while it holds fewer than 13 bits instead of 12
+    with planted("if (lane_pos(t, j, K) >= nk || have[j] >= 12) continue;",
+                 "if (lane_pos(t, j, K) >= nk || have[j] >= 13) continue;") as orc:
+        assert _w7_mismatches(orc, g, t, msg)[0] != []
+
+
 def test_every_short_stream_round_trips():
     tables = [
         {0: 1, 1: 1},

@@ -77,6 +77,95 @@ def test_w2_container_hand_example():
     assert flags == 0 and np.array_equal(s, sym)
 
 
+def _w6_case():
+    g = read_golden("w6_two_lanes.txt")
+    n = parse_int(g["n"][0])
+    sym = np.zeros(n, np.uint8)                       # a = 0x00 everywhere ...
+    for p in g["positions_c"][0].split():
+        sym[int(p)] = 0xFF                            # ... c at these positions
+    for p in g["positions_b"][0].split():
+        sym[int(p)] = 0x01                            # ... b here
+    freq = _freq({0x00: 4000, 0x01: 80, 0xFF: 16})
+    scale = np.array([parse_int(g["scale_bits"][0])], dtype=np.uint32).view(np.float32)
+    return g, sym, freq, scale
+
+
+def _w6_encode(orc, g, sym, freq, scale):
+    return orc.encode(orc.DTYPE_INT8, 1, sym.size, sym, scale, freq,
+                      chunk_symbols=parse_int(g["chunk_symbols"][0]), lane_run=parse_int(g["lane_run"][0]))
+
+
+def _w6_mismatches(orc, c, g, sym):
+    """What in container c (and its decode) differs from the hand-worked W6."""
+    bad = []
+    h = orc.header(c)
+    st = c[h["off_states"]:h["off_states"] + 256].view(np.uint32)
+    if st[0] != parse_int(g["state_lane0"][0]) or st[1] != parse_int(g["state_lane1"][0]) \
+            or np.any(st[2:] != parse_int(g["state_other_lanes"][0])):
+        bad.append("states")
+    wc = int(c[h["off_dir"] + 8:h["off_dir"] + 12].view(np.uint32)[0])
+    if wc != parse_int(g["word_count"][0]):
+        bad.append("word count")
+    words = c[h["off_words"]:h["off_words"] + 16].view(np.uint16)
+    if list(words) != [parse_int(t) for t in g["words_padded"][0].split()]:
+        bad.append("words")
+    s, flags = orc.decode_symbols(c)
+    if flags or not np.array_equal(s, sym):
+        bad.append("decode")
+    return bad
+
+
+def test_w6_two_lanes_hand_example():
+    """Two lanes renormalise in one step (ascending-lane word order); lanes
+    >= 1 carry symbols at the positions of the lane-run map."""
+    g, sym, freq, scale = _w6_case()
+    c = _w6_encode(oracle, g, sym, freq, scale)
+    assert _w6_mismatches(oracle, c, g, sym) == []
+    out, flags = oracle.decode_dequant(c)
+    assert flags == 0
+    exp = np.where(sym == 0xFF, parse_int(g["bf16_c"][0]),
+                   np.where(sym == 0x01, parse_int(g["bf16_b"][0]), parse_int(g["bf16_a"][0])))
+    assert np.array_equal(out, exp.astype(np.uint16))
+
+
+W6_PLANTS = {
+    # encoder walks the lanes of a step upwards: the step's words come out in
+    # descending-lane order
+    "encoder lanes ascending": ("for (uint32_t jj = OR_LANES; jj-- > 0;) {",
+                                "for (uint32_t jj = 0; jj < OR_LANES; jj++) {"),
+    # lane j's run placed at j + 64 * (t mod K) instead of j * K + (t mod K)
+    "position map transposed": ("return (t / K) * (uint64_t)OR_LANES * K + (uint64_t)j * K + (t % K);",
+                                "return (t / K) * (uint64_t)OR_LANES * K + (t % K) * OR_LANES + j;"),
+}
+
+
+@pytest.mark.parametrize("plant", list(W6_PLANTS))
+def test_w6_catches_planted_mistakes(planted, plant):
+    g, sym, freq, scale = _w6_case()
+    with planted(*W6_PLANTS[plant]) as bad:
+        c = _w6_encode(bad, g, sym, freq, scale)
+        assert _w6_mismatches(bad, c, g, sym) != []
+
+
+def test_w6_catches_descending_decoder(planted):
+    """A decoder that serves the renormalising lanes of a step in descending
+    order misreads the hand-worked container."""
+    g, sym, freq, scale = _w6_case()
+    c = _w6_encode(oracle, g, sym, freq, scale)
+    assert _w6_mismatches(oracle, c, g, sym) == []
+    old = ("        for (uint32_t j = 0; j < OR_LANES; j++) {\n"
+           "            uint64_t p = lane_pos(t, j, K);\n"
+           "            if (p >= nk) continue;\n"
+           "            uint8_t s = s2s[x[j] % OR_M];")
+    new = ("        for (uint32_t j = OR_LANES; j-- > 0;) {\n"
+           "            uint64_t p = lane_pos(t, j, K);\n"
+           "            if (p >= nk) continue;\n"
+           "            uint8_t s = s2s[x[j] % OR_M];")
+    with planted(old, new) as bad:
+        s, flags = bad.decode_symbols(c)
+        assert flags != 0 or not np.array_equal(s, sym)
+
+
 # ---------------------------------------------------------------------------
 # Exhaustive: C(D(x)) = x over every state, with renormalisation words
 # ---------------------------------------------------------------------------
