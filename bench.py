@@ -4,7 +4,7 @@
 Workload (the block the metric is quoted on): q, o 8192x8192; k, v 1024x8192;
 gate, up 28672x8192; down 8192x28672 -- 855,638,016 int8 weights whose codes
 are a 2.1-bit discrete Laplace, one 12-bit frequency table per tensor, fp32
-per-row scales, 4 super-weight escapes in down, container v1 with 64 Ki-symbol
+per-row scales, 4 super-weight escapes in down, container v1 with 32 Ki-symbol
 chunks and lane run 8. A step is one eq_decode_dequant_bf16 call over the
 whole block (one kernel launch) into a 1.71 GB bf16 buffer; containers are
 resident in HBM before timing starts.
@@ -109,11 +109,13 @@ def counter_record(name: str, key: str, kernel_src: str):
 
 
 def build_block(cfg: int, layer: int = 0, lane_run: int = 8, use_cache: bool = True,
-                tensors=None, whole_rows: bool = False, codec: int = 0, bits: float | None = None):
+                tensors=None, whole_rows: bool = False, codec: int = 0, bits: float | None = None,
+                chunk: int | None = None):
     """Encode one block with the library's host encoder and place its
     containers in device memory (all tensors, or the listed indices). Chunks
-    are 64 Ki symbols, or with whole_rows the nearest multiple of the row
-    length (what the fused decode + GEMV needs). codec 0 = rANS, 1 = Huffman.
+    are the configuration's size (synth.config_chunk) or `chunk` symbols, or
+    with whole_rows the multiple of the row length nearest to that size (what
+    the fused decode + GEMV needs). codec 0 = rANS, 1 = Huffman.
     With EQ_BENCH_CACHE=<dir> the encoded containers are kept there as .npy
     files and reused. bits: another entropy for the synthetic codes (bits
     per weight) than the configuration's."""
@@ -129,7 +131,8 @@ def build_block(cfg: int, layer: int = 0, lane_run: int = 8, use_cache: bool = T
     for i, sp in enumerate(specs):
         if tensors is not None and i not in tensors:
             continue
-        Z = whole_row_chunk(sp.cols, lane_run) if whole_rows else synth.CHUNK_SYMBOLS
+        target = chunk or synth.config_chunk(cfg)
+        Z = whole_row_chunk(sp.cols, lane_run, target) if whole_rows else target
         btag = "" if bits is None else f"_b{bits:g}"
         path = (os.path.join(cache, f"cfg{cfg}_layer{layer}_t{i}_k{lane_run}_z{Z}_c{codec}{btag}.npy")
                 if cache else None)
@@ -278,7 +281,8 @@ def bench_block(args):
     cfg, what = WORKLOADS[args.workload]
     codec = CODECS[args.codec]
     t0 = time.perf_counter()
-    specs, conts = build_block(cfg, 0, args.lane_run, codec=codec, bits=args.bits)
+    specs, conts = build_block(cfg, 0, args.lane_run, codec=codec, bits=args.bits, chunk=args.chunk)
+    Z = int(conts[0].hdr.chunk_symbols)
     offs = synth.block_offsets(specs)
     n = offs[-1]
     log(f"block built in {time.perf_counter() - t0:.1f} s: {n} weights, "
@@ -336,7 +340,7 @@ def bench_block(args):
         "dtype": "u32/f32",
         "data": "synthetic",
         "config": {
-            "workload": f"{what}; {args.codec} codec, 64Ki-symbol chunks, 64 lanes, K={args.lane_run}, bf16 out"
+            "workload": f"{what}; {args.codec} codec, {Z // 1024} Ki-symbol chunks, 64 lanes, K={args.lane_run}, bf16 out"
                         + ("" if args.bits is None else f"; codes drawn at {args.bits:g} bits per weight"),
             "codec": args.codec,
             "weights": n,
@@ -380,7 +384,7 @@ def bench_gemv(args):
     from rans_decode_amd import eq
 
     t0 = time.perf_counter()
-    specs, conts = build_block(4, 0, args.lane_run, whole_rows=True)
+    specs, conts = build_block(4, 0, args.lane_run, whole_rows=True, chunk=args.chunk)
     offs = synth.block_offsets(specs)
     n = offs[-1]
     log(f"block built in {time.perf_counter() - t0:.1f} s (whole-row chunks)")
@@ -491,6 +495,7 @@ def bench_encode(args):
 
     codec = CODECS[args.codec]
     specs = synth.config_specs(4)
+    Z4 = args.chunk or synth.config_chunk(4)
     tensors = []
     t0 = time.perf_counter()
     for i, sp in enumerate(specs):
@@ -503,10 +508,10 @@ def bench_encode(args):
             code=t.esc_code if esc else 0))
     log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
     # one workspace per tensor: the seven calls can run on seven streams
-    wss = [torch.empty(int(eq._lib.eq_encode_device_workspace(sp.rows, sp.cols, synth.CHUNK_SYMBOLS)),
+    wss = [torch.empty(int(eq._lib.eq_encode_device_workspace(sp.rows, sp.cols, Z4)),
                        dtype=torch.uint8, device="cuda") for sp in specs]
     streams = [torch.cuda.Stream() for _ in specs]  # default priority
-    outs = [torch.empty(int(eq._lib.eq_encode_device_bound(sp.rows, sp.cols, synth.CHUNK_SYMBOLS, sp.n_esc)),
+    outs = [torch.empty(int(eq._lib.eq_encode_device_bound(sp.rows, sp.cols, Z4, sp.n_esc)),
                         dtype=torch.uint8, device="cuda") for sp in specs]
     stream = torch.cuda.current_stream()
     # per-tensor length words and status flags, allocated once (flags of all
@@ -522,7 +527,7 @@ def bench_encode(args):
         for d, o, ln, st, w, st_ in zip(tensors, outs, lens, stats, wss, streams):
             sp = d["spec"]
             eq.eq_encode_device(sp.dtype, sp.rows, sp.cols, d["sym"], d["sc"], d["ei"], d["ev"],
-                                d["code"], synth.CHUNK_SYMBOLS, args.lane_run, workspace=w,
+                                d["code"], Z4, args.lane_run, workspace=w,
                                 out=o, stream=st_ if concurrent else stream, d_len=ln, d_status=st,
                                 codec=codec)
         if concurrent:
@@ -535,7 +540,7 @@ def bench_encode(args):
     if any(int(st.item()) for st in stats):
         raise RuntimeError("device encode flagged its input")
     # byte-for-byte against the host encoder (its containers, built or cached)
-    _, host = build_block(4, 0, args.lane_run, codec=codec)
+    _, host = build_block(4, 0, args.lane_run, codec=codec, chunk=Z4)
     for i, (c, o, ln) in enumerate(zip(host, outs, lens)):
         got = o[:int(ln.item())].cpu().numpy()
         if got.size != c.host.size or not np.array_equal(got, c.host):
@@ -572,7 +577,7 @@ def bench_encode(args):
         tab = eq.build_tables(t.symbols)
         eq.encode_host(tab, sp.dtype, sp.rows, sp.cols, t.symbols, t.scales, t.esc_idx if esc else None,
                        t.esc_val if esc else None, esc_code=t.esc_code if esc else 0,
-                       chunk_symbols=synth.CHUNK_SYMBOLS, lane_run=args.lane_run, codec=codec)
+                       chunk_symbols=Z4, lane_run=args.lane_run, codec=codec)
         host_enc_s += time.perf_counter() - t_enc0
         del t
     n = sum(sp.n for sp in specs)
@@ -589,7 +594,7 @@ def bench_encode(args):
         "warmup": args.warmup, "ms_per_step": round(f, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "u32", "data": "synthetic",
         "config": {"workload": "70B-shaped block, 855,638,016 int8 codes (2.1-bit Laplace), 4 super weights, "
-                               f"64 Ki chunks, K={args.lane_run}; {args.codec} codec; one eq_encode_device call per "
+                               f"{Z4 // 1024} Ki chunks, K={args.lane_run}; {args.codec} codec; one eq_encode_device call per "
                                "tensor, the seven on seven HIP streams",
                    "weights": n},
         "kernel_ms": {"mean": round(f, 4), "median": round(float(np.median(ms)), 4),
@@ -709,7 +714,7 @@ def bench_model(args):
     blocks, xs, ys = [], [], []
     comp_bytes = 0
     for layer in range(L):
-        _, conts = build_block(5, layer, args.lane_run, use_cache=False)
+        _, conts = build_block(5, layer, args.lane_run, use_cache=False, chunk=args.chunk)
         comp_bytes += algorithmic_bytes(conts)[0]
         blocks.append(eq.Block(conts, offs[:-1], None))
         xs.append([torch.from_numpy(synth.gemv_activation(5, layer, i, sp.cols)).to(torch.bfloat16).cuda()
@@ -787,7 +792,8 @@ def bench_model(args):
     t1 = time.perf_counter()
     fblocks = []
     for layer in range(L):
-        _, dconts = build_block(5, layer, args.lane_run, use_cache=False, tensors=[6], whole_rows=True)
+        _, dconts = build_block(5, layer, args.lane_run, use_cache=False, tensors=[6], whole_rows=True,
+                                chunk=args.chunk)
         fblocks.append(eq.Block(blocks[layer].containers[:6] + dconts, offs[:-1], None))
     log(f"whole-row down_proj containers built in {time.perf_counter() - t1:.0f} s")
     yf = [[torch.empty_like(y) for y in yl] for yl in ys]
@@ -859,6 +865,9 @@ def main():
                     help="block workloads: entropy of the synthetic codes in bits per weight "
                          "(default: the configuration's)")
     ap.add_argument("--layers", type=int, default=80, help="blocks in the model80 workload")
+    ap.add_argument("--chunk", type=int, default=None,
+                    help="symbols per chunk of the encoded containers (default: the configuration's; "
+                         "whole-row containers take the nearest multiple of the row length)")
     ap.add_argument("--codec", choices=sorted(CODECS), default="rans",
                     help="entropy coder of the block workloads' containers (rANS: EntQuant's ANS; "
                          "huffman: EntroLLM's coder, for comparison)")

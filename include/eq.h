@@ -181,6 +181,16 @@ typedef struct eq_block {
 eq_status eq_build_tables(const uint8_t *symbols, uint64_t n, eq_tables *out);
 
 /*
+ * eq_tables_from_freq -- an eq_tables for a given 12-bit frequency table (any
+ * valid table, not necessarily the quantiser's): copies freq and derives the
+ * cumulative frequencies cum (counts and n are zero). The metadata half of
+ * technical component 2 of the EntQuant summary, for callers that bring
+ * their own table. freq: host array of 256 entries summing to 4096.
+ * Errors: EQ_EINVAL (NULL, or the entries do not sum to 4096).
+ */
+eq_status eq_tables_from_freq(const uint16_t *freq, eq_tables *out);
+
+/*
  * eq_encode_host -- offline ANS encoding of one tensor into container v1
  * (technical component 2 of the EntQuant summary: flatten, ANS-compress,
  * store bitstream + scales + metadata). Host only, multi-threaded over chunks.
@@ -312,12 +322,16 @@ eq_status eq_gemv_bf16(const uint16_t *d_w, uint64_t rows, uint64_t cols, const 
  * buffers on decode_stream while gemv_stream runs each decoded block's
  * GEMVs on the other buffer; events gate buffer reuse.
  *
- * eq_pipeline_create makes a plan holding 2 * n_blocks + 2 HIP events (no
- * device memory). eq_pipeline_run enqueues one pass: for block b, decode into
+ * eq_pipeline_create makes a plan holding 2 * n_blocks + 1 HIP events (no
+ * device memory). eq_pipeline_run enqueues one pass: decode_stream first
+ * waits for everything already enqueued on gemv_stream (a previous run's
+ * GEMVs may still read either buffer); then for block b, decode into
  * buf[b % 2] after the GEMVs of block b - 2 finished, then the GEMVs of
  * block b (tensor i: W = buf[b % 2] + tensors[i].out_offset, rows/cols from
- * its header, x = d_x[b][i], y = d_y[b][i]) after that decode. The run ends
- * with gemv_stream waiting for nothing else; the caller synchronises.
+ * its header, x = d_x[b][i], y = d_y[b][i]) after that decode. The last
+ * GEMVs are on gemv_stream: the y of a run are complete once gemv_stream
+ * reaches the end of that run (an event recorded there, or a synchronise);
+ * runs may be enqueued back to back without a synchronise.
  * d_x / d_y: host arrays of n_blocks pointers to host arrays of device
  * pointers (one per tensor). Errors: EQ_EINVAL, EQ_EHIP.
  */

@@ -56,9 +56,6 @@ namespace {
 #ifndef EQ_LUT_SCAN
 #define EQ_LUT_SCAN 1   // slot table by a running maximum of start marks (else a binary search per slot)
 #endif
-#ifndef EQ_LUT8
-#define EQ_LUT8 1
-#endif
 #ifndef EQ_RENORM_EXEC
 #define EQ_RENORM_EXEC 1
 #endif
@@ -164,9 +161,10 @@ __device__ __forceinline__ XRun<K> load_x(const uint16_t *x) {
     return r;
 }
 
-#if EQ_LUT8
-// 8-byte slot-table entry: lo = f | symbol << 24 (bits 12..23 zero, so a
-// 24-bit multiply sees f alone), hi = slot - cum.
+// 8-byte slot-table entry: lo = f | symbol << 24, hi = slot - cum. f is at
+// most 4096 (a segment of an adaptive-table container can hold one symbol),
+// so it fits bits 0..12 and bits 13..23 are zero: a 24-bit multiply by lo
+// sees f alone.
 typedef uint2 LutEnt;
 constexpr int kSymShift = 24;
 __device__ __forceinline__ uint32_t ent_bits(LutEnt e) { return e.x; }
@@ -176,18 +174,6 @@ __device__ __forceinline__ LutEnt make_ent(uint32_t s, uint32_t f, uint32_t bias
 __device__ __forceinline__ uint32_t ent_next(LutEnt e, uint32_t x) {
     return __umul24(e.x, x >> 12) + e.y;
 }
-#else
-// 4-byte slot-table entry: symbol | f << 8 | (slot - cum) << 20.
-typedef uint32_t LutEnt;
-constexpr int kSymShift = 0;
-__device__ __forceinline__ uint32_t ent_bits(LutEnt e) { return e; }
-__device__ __forceinline__ LutEnt make_ent(uint32_t s, uint32_t f, uint32_t bias) {
-    return s | (f << 8) | (bias << 20);
-}
-__device__ __forceinline__ uint32_t ent_next(LutEnt e, uint32_t x) {
-    return __umul24((e >> 8) & 0xFFFu, x >> 12) + (e >> 20);
-}
-#endif
 
 // Value of the symbol byte held in a slot-table entry's bits kSymShift..+8.
 template <uint32_t DT>
@@ -206,9 +192,10 @@ __device__ __forceinline__ void raise_flag(uint32_t *status, uint32_t bits, uint
     if (status && bits && lane == 0) atomicOr(status, bits);
 }
 
-// Slot table of the tensor: for every slot in [0, 4096) the byte s with
-// cum[s] <= slot < cum[s] + f[s], packed as s | f << 8 | (slot - cum[s]) << 20
-// (f <= 4095 here; a one-symbol tensor never builds a table).
+// Slot table of the tensor (or of one segment's table): for every slot in
+// [0, 4096) the byte s with cum[s] <= slot < cum[s] + f[s], as the entry
+// (f[s], s, slot - cum[s]). A one-symbol tensor never builds a table; a
+// one-symbol segment does, with f = 4096 in every entry.
 __device__ __forceinline__ void build_lut(const uint16_t *freq, LutEnt *lut, uint32_t *scr) {
     const uint32_t tid = threadIdx.x;
     uint32_t *cum = scr;  // [257]
@@ -959,8 +946,11 @@ __device__ __forceinline__ void const_chunk_gemv(const TArgs &T, uint64_t chunk,
 // Output kinds of the decode kernel.
 enum : int { OUT_U8 = 0, OUT_BF16 = 1, OUT_GEMV = 2 };
 
+// (the slot table and rings of three workgroups fill a CU's LDS: six waves
+// per SIMD, which the register allocation must not undercut)
 template <int K, int OUT>
-__global__ void __launch_bounds__(kThreads) k_decode(LArgs a) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6)))
+k_decode(LArgs a) {
     constexpr bool BF16 = OUT != OUT_U8;
     constexpr bool GEMV = OUT == OUT_GEMV;
     __shared__ LutEnt lut[4096];
@@ -1223,6 +1213,7 @@ eq_status launch_block(const eq_block *b, void *out, const uint16_t *const *x, f
 struct eq_pipeline {
     uint32_t n_blocks;
     std::vector<hipEvent_t> decoded, consumed;
+    hipEvent_t start;  // gemv_stream's position when a run begins
 };
 
 extern "C" {
@@ -1269,6 +1260,12 @@ eq_status eq_pipeline_create(uint32_t n_blocks, eq_pipeline **out) {
     p->n_blocks = n_blocks;
     p->decoded.assign(n_blocks, nullptr);
     p->consumed.assign(n_blocks, nullptr);
+    p->start = nullptr;
+    if (hipEventCreateWithFlags(&p->start, hipEventDisableTiming) != hipSuccess) {
+        p->start = nullptr;
+        eq_pipeline_destroy(p);
+        return EQ_EHIP;
+    }
     for (uint32_t i = 0; i < n_blocks; ++i) {
         if (hipEventCreateWithFlags(&p->decoded[i], hipEventDisableTiming) != hipSuccess ||
             hipEventCreateWithFlags(&p->consumed[i], hipEventDisableTiming) != hipSuccess) {
@@ -1287,6 +1284,10 @@ eq_status eq_pipeline_run(eq_pipeline *p, const eq_block *blocks, uint32_t n_blo
     hipStream_t ds = static_cast<hipStream_t>(decode_stream);
     hipStream_t gs = static_cast<hipStream_t>(gemv_stream);
     uint16_t *buf[2] = {d_buf0, d_buf1};
+    // the first two decodes overwrite buffers that GEMVs enqueued earlier on
+    // gemv_stream (a previous run's last blocks) may still be reading
+    if (hipEventRecord(p->start, gs) != hipSuccess || hipStreamWaitEvent(ds, p->start, 0) != hipSuccess)
+        return EQ_EHIP;
     for (uint32_t b = 0; b < n_blocks; ++b) {
         uint16_t *dst = buf[b & 1u];
         if (b >= 2 && hipStreamWaitEvent(ds, p->consumed[b - 2], 0) != hipSuccess) return EQ_EHIP;
@@ -1311,6 +1312,7 @@ eq_status eq_pipeline_destroy(eq_pipeline *p) {
         if (e) (void)hipEventDestroy(e);
     for (hipEvent_t e : p->consumed)
         if (e) (void)hipEventDestroy(e);
+    if (p->start) (void)hipEventDestroy(p->start);
     delete p;
     return EQ_OK;
 }

@@ -328,6 +328,19 @@ eq_status eq_build_tables(const uint8_t *symbols, uint64_t n, eq_tables *out) {
     return EQ_OK;
 }
 
+eq_status eq_tables_from_freq(const uint16_t *freq, eq_tables *out) {
+    if (!freq || !out) return EQ_EINVAL;
+    uint32_t sum = 0;
+    for (int s = 0; s < 256; ++s) sum += freq[s];
+    if (sum != eqfmt::kProbScale) return EQ_EINVAL;
+    std::memset(out, 0, sizeof *out);
+    for (int s = 0; s < 256; ++s) {
+        out->freq[s] = freq[s];
+        out->cum[s + 1] = out->cum[s] + freq[s];
+    }
+    return EQ_OK;
+}
+
 eq_status eq_encode_host(const eq_tables *t, const eq_tensor_desc *d, const uint8_t *symbols,
                          const float *scales, const uint64_t *esc_idx, const uint16_t *esc_bf16,
                          uint64_t n_esc, void *out, uint64_t cap, uint64_t *out_len) {

@@ -4,7 +4,7 @@ Every step of the decode runs in the library's HIP kernels; PyTorch provides
 device memory and streams. There is no CPU fallback: if libeq.so is missing
 or cannot be loaded, importing this module raises.
 
-The functions keep the C names (``eq_build_tables``, ``eq_encode_host``,
+The functions keep the C names (``eq_build_tables``, ``eq_tables_from_freq``, ``eq_encode_host``,
 ``eq_parse_header``, ``eq_decode_block``, ``eq_decode_dequant_bf16``,
 ``eq_decode_gemv_bf16``, ``eq_gemv_bf16``, ``eq_pipeline_*``, ``eq_bf16_from_f32``) as thin wrappers
 over numpy / torch arrays, plus a few conveniences (``build_tables``,
@@ -70,6 +70,7 @@ def _load():
     P = ctypes.POINTER
     sig = {
         "eq_build_tables": [_vp, _u64, P(eq_tables)],
+        "eq_tables_from_freq": [_vp, P(eq_tables)],
         "eq_encode_host": [P(eq_tables), P(eq_tensor_desc), _vp, _vp, _vp, _vp, _u64, _vp, _u64, P(_u64)],
         "eq_parse_header": [_vp, _u64, P(eq_header)],
         "eq_decode_block": [P(eq_block), _vp, _vp],
@@ -134,18 +135,18 @@ def eq_build_tables(symbols: np.ndarray) -> eq_tables:
 build_tables = eq_build_tables
 
 
-def tables_from_freq(freq) -> eq_tables:
-    """A custom table (any valid 12-bit frequencies) in eq_tables form."""
+def eq_tables_from_freq(freq) -> eq_tables:
+    """A custom table (any valid 12-bit frequencies) in eq_tables form; the
+    library derives the cumulative frequencies."""
     f = np.ascontiguousarray(freq, dtype=np.uint16)
+    if f.size != 256:
+        raise ValueError("a frequency table has 256 entries")
     t = eq_tables()
-    for s in range(256):
-        t.freq[s] = int(f[s])
-    c = 0
-    for s in range(256):
-        t.cum[s] = c
-        c += int(f[s])
-    t.cum[256] = c
+    _check("eq_tables_from_freq", _lib.eq_tables_from_freq(f.ctypes.data, ctypes.byref(t)))
     return t
+
+
+tables_from_freq = eq_tables_from_freq
 
 
 def eq_encode_host(tables: eq_tables, desc: eq_tensor_desc, symbols: np.ndarray, scales: np.ndarray,
@@ -350,7 +351,13 @@ def eq_encode_device(dtype: int, rows: int, cols: int, d_symbols, d_scales, d_es
     """Device-side encode (torch tensors on the GPU). Returns (out, d_len,
     d_status) without synchronising: out[:int(d_len)] is the container once
     the stream has run. A d_status passed in is not cleared (flags of
-    several calls accumulate)."""
+    several calls accumulate).
+
+    Lifetimes: the kernels run on `stream` (default: the current stream).
+    Buffers this function allocates (workspace, out, d_len, d_status when not
+    given) are marked as used on `stream`, so torch's caching allocator does
+    not hand their memory out again before the kernels finish. Buffers the
+    caller passes stay the caller's to keep alive until then."""
     torch = _torch()
     n_esc = 0 if d_esc_idx is None else int(d_esc_idx.numel())
     d = eq_tensor_desc(dtype=dtype, lane_run=lane_run, rows=rows, cols=cols,
@@ -359,14 +366,24 @@ def eq_encode_device(dtype: int, rows: int, cols: int, d_symbols, d_scales, d_es
     dev = d_symbols.device
     wsb = int(_lib.eq_encode_device_workspace(rows, cols, chunk_symbols))
     cap = int(_lib.eq_encode_device_bound(rows, cols, chunk_symbols, n_esc))
+    made = []
     if workspace is None:
         workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+        made.append(workspace)
     if out is None:
         out = torch.empty(max(cap, 16), dtype=torch.uint8, device=dev)
+        made.append(out)
     if d_len is None:
         d_len = torch.zeros(1, dtype=torch.int64, device=dev)
+        made.append(d_len)
     if d_status is None:
         d_status = torch.zeros(1, dtype=torch.int32, device=dev)
+        made.append(d_status)
+    if made and stream is not None and not isinstance(stream, int) and stream != torch.cuda.current_stream(dev):
+        for t in made:
+            t.record_stream(stream)
+        # the zero fills above ran on the current stream: the encode must see them
+        stream.wait_stream(torch.cuda.current_stream(dev))
     _check("eq_encode_device", _lib.eq_encode_device(
         ctypes.byref(d), d_symbols.data_ptr(), d_scales.data_ptr(),
         d_esc_idx.data_ptr() if n_esc else None, d_esc_val.data_ptr() if n_esc else None, n_esc,

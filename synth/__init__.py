@@ -249,6 +249,16 @@ CHUNK_SYMBOLS = 65536
 LANE_RUN = 8
 N_LAYERS_MODEL = 80
 
+# Chunk size of each configuration's containers (symbols per chunk). The
+# 4096x4096 matrix mandates 64 Ki; elsewhere the size is a container field,
+# chosen by measured decode time against the 256 B of lane states each chunk
+# adds: smaller chunks shorten the serial work of the last waves of a launch.
+CONFIG_CHUNK = {1: 16384, 2: 65536, 3: 16384, 4: 32768, 5: 32768}
+
+
+def config_chunk(cfg: int) -> int:
+    return CONFIG_CHUNK[cfg]
+
 
 def config_specs(cfg: int) -> list[TensorSpec]:
     if cfg == 1:
