@@ -196,6 +196,51 @@ def sample(cat: Categorical, key: int, start: int, n: int, threads: int | None =
     return out
 
 
+GPU_LIB_PATH = os.path.join(_HERE, "libsynth_gpu.so")
+
+
+@lru_cache(maxsize=1)
+def _gpu_lib():
+    if not os.path.exists(GPU_LIB_PATH):
+        raise RuntimeError(f"{GPU_LIB_PATH} is missing: run __graft_entry__.build() first")
+    lib = ctypes.CDLL(GPU_LIB_PATH)
+    lib.synth_categorical_gpu.restype = ctypes.c_int
+    lib.synth_categorical_gpu.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    return lib
+
+
+def sample_gpu(cat: Categorical, key: int, start: int, out, stream=None) -> None:
+    """The bytes `sample` draws for stream indices start .. start+out.numel()-1,
+    drawn on the GPU into the uint8 device tensor `out` (same values)."""
+    import torch
+    dev = out.device
+    syms = torch.from_numpy(cat.syms).to(dev)
+    thr = torch.from_numpy(cat.thr.view(np.int64)).to(dev)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    rc = _gpu_lib().synth_categorical_gpu(key, start, out.numel(), syms.data_ptr(), thr.data_ptr(),
+                                          len(cat.syms), out.data_ptr(), s.cuda_stream)
+    if rc:
+        raise RuntimeError("synth_categorical_gpu failed")
+    s.synchronize()  # the category tables are freed on return
+
+
+def make_tensor_gpu(cfg: int, layer: int, t: int, out, spec: TensorSpec | None = None) -> Tensor:
+    """make_tensor with the symbols drawn on the GPU into the uint8 device
+    tensor `out` (spec.n elements): the returned Tensor carries the scales
+    and the super-weight list, and symbols = None."""
+    import torch
+    spec = spec or config_specs(cfg)[t]
+    if out.numel() != spec.n or out.dtype != torch.uint8:
+        raise ValueError("out must be a uint8 device tensor of spec.n elements")
+    sample_gpu(table_for(spec), stream_key(cfg, layer, t, PURPOSE_SYMBOLS), 0, out)
+    tensor = Tensor(spec, None, scales_for(cfg, layer, t, spec.rows))
+    if spec.n_esc:
+        tensor.esc_idx, tensor.esc_val = escapes_for(cfg, layer, t, spec)
+        out[torch.from_numpy(tensor.esc_idx.astype(np.int64)).to(out.device)] = ESC_CODE[spec.dtype]
+    return tensor
+
+
 def empirical_entropy(sym: np.ndarray) -> float:
     c = np.bincount(sym, minlength=256).astype(np.float64)
     p = c[c > 0] / c.sum()

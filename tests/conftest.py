@@ -18,6 +18,7 @@ def pytest_configure(config):
 
 def _ensure_built():
     libs = [os.path.join(ROOT, "oracle", "liboracle.so"), os.path.join(ROOT, "synth", "libsynth.so"),
+            os.path.join(ROOT, "synth", "libsynth_gpu.so"),
             os.path.join(ROOT, "rans_decode_amd", "libeq.so")]
     if not all(os.path.exists(p) for p in libs):
         import __graft_entry__

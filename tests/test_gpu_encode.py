@@ -1,11 +1,13 @@
-"""GPU device-side encoder (`eq_encode_device`) against the host encoder:
-the containers must be byte-identical to eq_encode_host(eq_build_tables(s))
-(which the CPU tests pin byte-for-byte to the oracle's encoder), and a
-GPU decode of them must reproduce the original symbols."""
+"""GPU device-side encoder (`eq_encode_device`) against the oracle: every
+container must be byte-identical to the oracle's encoder run on the oracle's
+own tables (its frequency quantiser, its length-limited Huffman code, its
+per-segment quantiser), and a GPU decode of it must reproduce the original
+symbols. The host encoder's container is compared too, as an extra check."""
 import numpy as np
 import pytest
 import torch
 
+import oracle
 import synth
 from conftest import gpu_available
 from gpu_util import assert_same, log, run_u8
@@ -40,14 +42,37 @@ def host_container(sym, scales, dtype, rows, cols, Z, K, esc_idx=None, esc_val=N
                           esc_code=esc_code, chunk_symbols=Z, lane_run=K, codec=codec, seg_chunks=seg)
 
 
+def oracle_container(sym, scales, dtype, rows, cols, Z, K, esc_idx=None, esc_val=None, esc_code=0,
+                     codec=0, seg=0):
+    """The oracle's container on the oracle's own tables."""
+    esc = esc_idx is not None and len(esc_idx) > 0
+    if codec == eq.EQ_CODEC_HUFFMAN:
+        table = oracle.huff_lengths(np.bincount(sym, minlength=256).astype(np.uint64))
+    elif seg:
+        n_chunks = -(-sym.size // Z)
+        table = np.stack([oracle.build_freq(sym[g * seg * Z:(g + 1) * seg * Z])
+                          for g in range(-(-n_chunks // seg))])
+    else:
+        table = oracle.build_freq(sym)
+    return oracle.encode(dtype, rows, cols, sym, scales, table, Z, K, esc_enabled=esc or esc_code != 0,
+                         esc_code=esc_code, esc_idx=esc_idx if esc else None, esc_val=esc_val if esc else None,
+                         codec=codec, seg_chunks=seg)
+
+
+def _same_bytes(got, exp, what):
+    assert got.size == exp.size, f"{what}: size {got.size} vs {exp.size}"
+    bad = np.flatnonzero(got != exp)
+    assert bad.size == 0, f"{what}: {bad.size} bytes differ, first at {bad[0]}"
+
+
 def check_equal(sym, scales, dtype, rows, cols, Z=65536, K=8, esc_idx=None, esc_val=None, esc_code=0,
                 what="", codec=0, seg=0):
     got, st = device_container(sym, scales, dtype, rows, cols, Z, K, esc_idx, esc_val, esc_code, codec, seg)
     assert st == 0, f"{what}: device status {st}"
-    exp = host_container(sym, scales, dtype, rows, cols, Z, K, esc_idx, esc_val, esc_code, codec, seg)
-    assert got.size == exp.size, f"{what}: size {got.size} vs {exp.size}"
-    bad = np.flatnonzero(got != exp)
-    assert bad.size == 0, f"{what}: {bad.size} bytes differ, first at {bad[0]}"
+    _same_bytes(got, oracle_container(sym, scales, dtype, rows, cols, Z, K, esc_idx, esc_val, esc_code, codec,
+                                      seg), f"{what} vs the oracle")
+    _same_bytes(got, host_container(sym, scales, dtype, rows, cols, Z, K, esc_idx, esc_val, esc_code, codec, seg),
+                f"{what} vs the host encoder")
     return got
 
 
@@ -66,11 +91,12 @@ def test_block_tensors_with_escapes_and_e4m3():
     for cfg, i in [(4, 6), (4, 1), (3, 0), (3, 5)]:
         t = synth.make_tensor(cfg, 0, i)
         sp = t.spec
-        log(f"case device encode config {cfg} tensor {sp.name}")
         esc = t.esc_idx.size > 0
-        check_equal(t.symbols, t.scales, sp.dtype, sp.rows, sp.cols,
-                    esc_idx=t.esc_idx if esc else None, esc_val=t.esc_val if esc else None,
-                    esc_code=t.esc_code if esc else 0, what=f"cfg {cfg} {sp.name}")
+        for Z in sorted({synth.config_chunk(cfg), 65536}):
+            log(f"case device encode config {cfg} tensor {sp.name}, chunk {Z}")
+            check_equal(t.symbols, t.scales, sp.dtype, sp.rows, sp.cols, Z=Z,
+                        esc_idx=t.esc_idx if esc else None, esc_val=t.esc_val if esc else None,
+                        esc_code=t.esc_code if esc else 0, what=f"cfg {cfg} {sp.name} Z={Z}")
         del t
 
 

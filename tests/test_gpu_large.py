@@ -88,6 +88,10 @@ def test_tensor_of_more_than_2pow32_elements():
     assert int(dst.item()) == 0
     got_blob = dout[:int(dlen.item())].cpu().numpy()
     assert got_blob.size == blob.size and np.array_equal(got_blob, blob)
+    log("case tensor beyond 2^32: the oracle's container")
+    ref = oracle.encode(spec.dtype, spec.rows, spec.cols, t.symbols, t.scales, oracle.build_freq(t.symbols),
+                        esc_enabled=True, esc_code=code, esc_idx=esc_idx, esc_val=esc_val)
+    assert ref.size == got_blob.size and np.array_equal(ref, got_blob)
 
 
 def test_outputs_beyond_element_2pow32():

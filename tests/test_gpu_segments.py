@@ -76,3 +76,28 @@ def test_fused_gemv_and_mixed_block():
     assert st == 0
     for tt, o in zip(tensors, offs):
         assert_same(got[o:o + tt.spec.n], expected_bf16(tt), "mixed")
+
+
+def test_single_symbol_segment():
+    """A segment whose chunks hold one byte only: its table has f = 4096 in
+    every slot-table entry (the other segments are ordinary); decode to
+    bytes, bf16 and the fused GEMV against the oracle."""
+    rng = np.random.default_rng(17)
+    rows, cols, Z, K, seg = 64, 8192, 8192, 8, 8
+    spec = synth.TensorSpec("t", rows, cols, synth.DTYPE_INT8, 2.1, 0)
+    t = synth.make_tensor(4, 140, 0, spec=spec)
+    one = seg * Z                            # segment 1 = flat positions [one, 2 * one)
+    t.symbols[one:2 * one] = 0x03
+    t.scales = rng.uniform(0.005, 0.015, rows).astype(np.float32)
+    blob = seg_encode(t, Z, K, seg)
+    h = eq.parse_header(blob)
+    tabs = blob[h.off_freq:h.off_freq + 512 * 4].view(np.uint16).reshape(4, 256)
+    assert tabs[1, 3] == 4096 and tabs[1].sum() == 4096 and np.count_nonzero(tabs[0]) > 1
+    log("case single-symbol segment")
+    c = _check(t, Z, K, seg, "single-symbol segment")
+    w = expected_bf16(t).reshape(rows, cols)
+    x = oracle.bf16_rne(rng.standard_normal(cols).astype(np.float32))
+    (y,), st = run_gemv([c], [x], [rows])
+    assert st == 0
+    check_close(y, w, x, "single-symbol segment gemv")
+    one_hot_exact(c, w, [0, 5000, cols - 1], "single-symbol segment gemv")
