@@ -87,7 +87,8 @@
  *  - Device errors found while decoding are ORed into *d_status as
  *    EQ_DEV_* bits; read them after synchronising. After such an error the
  *    output contents are unspecified.
- *  - Thread-safe and reentrant; no global mutable state.
+ *  - Thread-safe and reentrant; no global mutable state, except the per-GPU
+ *    scratch array of eq_encode_device_static (see there).
  */
 #ifndef EQ_H
 #define EQ_H
@@ -302,6 +303,27 @@ eq_status eq_encode_device(const eq_tensor_desc *d, const uint8_t *d_symbols, co
                            const uint64_t *d_esc_idx, const uint16_t *d_esc_bf16, uint64_t n_esc,
                            void *d_workspace, uint64_t workspace_bytes, void *d_out, uint64_t cap,
                            uint64_t *d_out_len, uint32_t *d_status, void *stream);
+
+/*
+ * eq_encode_device_static -- eq_encode_device without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation). The
+ * encoder's scratch is a static device array of
+ * EQ_ENCODE_STATIC_SCRATCH_BYTES that every GPU the library runs on holds
+ * until the process ends; the call allocates and frees nothing. Tensors whose
+ * eq_encode_device_workspace() exceeds that size (e.g. 28672 x 8192) get
+ * EQ_ERANGE; 8192 x 8192 and smaller fit.
+ * Arguments, output and errors as eq_encode_device; the stream must belong
+ * to the current device. Every call on one GPU shares that GPU's array and
+ * finds the previous call's contents in it (the kernels clear what they
+ * need): calls that overlap in time on one GPU (several streams or host
+ * threads) race and must be serialised by the caller.
+ */
+#define EQ_ENCODE_STATIC_SCRATCH_BYTES (136ull << 20)
+eq_status eq_encode_device_static(const eq_tensor_desc *d, const uint8_t *d_symbols, const float *d_scales,
+                                  const uint64_t *d_esc_idx, const uint16_t *d_esc_bf16, uint64_t n_esc,
+                                  void *d_out, uint64_t cap, uint64_t *d_out_len, uint32_t *d_status,
+                                  void *stream);
 
 /*
  * eq_gemv_bf16 -- y[r] = sum_c W[r, c] * x[c] for a row-major bf16 [rows,

@@ -35,7 +35,9 @@
 #include <hip/hip_runtime.h>
 #include <type_traits>
 
+#include <atomic>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/eq.h"
 #include "format.hpp"
@@ -995,6 +997,31 @@ __global__ void __launch_bounds__(kEncThreads) k_enc_copy(EncArgs a) {
     for (uint64_t i = esc_val + 2 * a.n_esc + threadIdx.x; i < total; i += blockDim.x) a.out[i] = 0;
 }
 
+// The encoder's scratch for callers that cannot allocate: one array per GPU,
+// held for the life of the process, shared by every call on that GPU.
+static __device__ __align__(256) uint8_t scratch[EQ_ENCODE_STATIC_SCRATCH_BYTES];
+
+// Device address of `scratch` on each GPU, looked up once per GPU with that
+// GPU current. The array's name in host code is only a stand-in for the
+// symbol: kernels get this address, never the name.
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+void *scratch_on_current_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+
 template <int K>
 void launch_chunks(uint32_t grid, hipStream_t s, const EncArgs &a) {
     if (a.codec == kCodecHuffman) hipLaunchKernelGGL(k_enc_hchunks<K>, dim3(grid), dim3(kEncThreads), 0, s, a);
@@ -1074,13 +1101,13 @@ eq_status eq_encode_device(const eq_tensor_desc *d, const uint8_t *d_symbols, co
     hipStream_t s = static_cast<hipStream_t>(stream);
     const uint32_t cgrid = (uint32_t)((n_chunks + kEncWaves - 1) / kEncWaves);
     if (n_chunks > 0xFFFFFFFFull / 4) return EQ_EINVAL;
+    if (a.n_tab > 65535) return EQ_EINVAL;
     hipLaunchKernelGGL(k_enc_check, dim3(64), dim3(256), 0, s, a);
     // one grid row per table; about 32 KiB of symbols per workgroup and pass,
     // at most kHistMaxGrid workgroups in all (and at least one per table)
     const uint64_t hg = (a.seg_syms + 32767) / 32768;
     const uint64_t hcap = kHistMaxGrid / a.n_tab ? kHistMaxGrid / a.n_tab : 1;
     const uint32_t hgrid = (uint32_t)(hg < hcap ? (hg ? hg : 1) : hcap);
-    if (a.n_tab > 65535) return EQ_EINVAL;
     hipLaunchKernelGGL(k_enc_hist, dim3(hgrid, (uint32_t)a.n_tab), dim3(256), 0, s, a);
     if (a.codec == kCodecHuffman) hipLaunchKernelGGL(k_enc_huff, dim3(1), dim3(512), 0, s, a);
     else hipLaunchKernelGGL(k_enc_quant, dim3((uint32_t)a.n_tab), dim3(256), 0, s, a);
@@ -1094,6 +1121,20 @@ eq_status eq_encode_device(const eq_tensor_desc *d, const uint8_t *d_symbols, co
     hipLaunchKernelGGL(k_enc_scan, dim3(1), dim3(1024), 0, s, a);
     hipLaunchKernelGGL(k_enc_copy, dim3(cgrid), dim3(kEncThreads), 0, s, a);
     return hipGetLastError() == hipSuccess ? EQ_OK : EQ_EHIP;
+}
+
+eq_status eq_encode_device_static(const eq_tensor_desc *d, const uint8_t *d_symbols, const float *d_scales,
+                                  const uint64_t *d_esc_idx, const uint16_t *d_esc_bf16, uint64_t n_esc,
+                                  void *d_out, uint64_t cap, uint64_t *d_out_len, uint32_t *d_status,
+                                  void *stream) {
+    if (!d || d->rows == 0 || d->cols == 0 || d->chunk_symbols == 0) return EQ_EINVAL;
+    const uint64_t need = eq_encode_device_workspace(d->rows, d->cols, d->chunk_symbols);
+    if (need == 0) return EQ_EINVAL;
+    if (need > EQ_ENCODE_STATIC_SCRATCH_BYTES) return EQ_ERANGE;
+    void *ws = scratch_on_current_device();
+    if (!ws) return EQ_EHIP;
+    return eq_encode_device(d, d_symbols, d_scales, d_esc_idx, d_esc_bf16, n_esc, ws,
+                            EQ_ENCODE_STATIC_SCRATCH_BYTES, d_out, cap, d_out_len, d_status, stream);
 }
 
 }  // extern "C"

@@ -82,6 +82,7 @@ def _load():
         "eq_pipeline_destroy": [_vp],
         "eq_bf16_from_f32": [_vp, _u64, _vp, _vp],
         "eq_encode_device": [P(eq_tensor_desc), _vp, _vp, _vp, _vp, _u64, _vp, _u64, _vp, _u64, _vp, _vp, _vp],
+        "eq_encode_device_static": [P(eq_tensor_desc), _vp, _vp, _vp, _vp, _u64, _vp, _u64, _vp, _vp, _vp],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -390,3 +391,23 @@ def eq_encode_device(dtype: int, rows: int, cols: int, d_symbols, d_scales, d_es
         workspace.data_ptr(), workspace.numel(), out.data_ptr(), out.numel(), d_len.data_ptr(),
         d_status.data_ptr(), _stream_handle(stream)))
     return out, d_len, d_status
+
+
+EQ_ENCODE_STATIC_SCRATCH_BYTES = 136 << 20
+
+
+def eq_encode_device_static(dtype: int, rows: int, cols: int, d_symbols, d_scales, out, d_len, d_status,
+                            d_esc_idx=None, d_esc_val=None, esc_code: int = 0, chunk_symbols: int = 65536,
+                            lane_run: int = 8, stream=None, codec: int = 0, seg_chunks: int = 0) -> None:
+    """eq_encode_device with the library's static per-GPU scratch instead of
+    a workspace: the caller passes every buffer (out of at least
+    eq_encode_device_bound bytes, d_len u64, d_status u32, all on the GPU),
+    and the call allocates nothing. Calls that overlap on one GPU race."""
+    n_esc = 0 if d_esc_idx is None else int(d_esc_idx.numel())
+    d = eq_tensor_desc(dtype=dtype, lane_run=lane_run, rows=rows, cols=cols,
+                       chunk_symbols=chunk_symbols, esc_enabled=1 if n_esc or esc_code else 0,
+                       esc_code=esc_code, codec=codec, seg_chunks=seg_chunks)
+    _check("eq_encode_device_static", _lib.eq_encode_device_static(
+        ctypes.byref(d), d_symbols.data_ptr(), d_scales.data_ptr(),
+        d_esc_idx.data_ptr() if n_esc else None, d_esc_val.data_ptr() if n_esc else None, n_esc,
+        out.data_ptr(), out.numel(), d_len.data_ptr(), d_status.data_ptr(), _stream_handle(stream)))
