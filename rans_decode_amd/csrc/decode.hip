@@ -53,9 +53,6 @@ namespace {
 #ifndef EQ_SADDR_STORE
 #define EQ_SADDR_STORE 1  // K = 8 bf16 stores with a scalar base address
 #endif
-#ifndef EQ_LUT_SCAN
-#define EQ_LUT_SCAN 1   // slot table by a running maximum of start marks (else a binary search per slot)
-#endif
 #ifndef EQ_RENORM_EXEC
 #define EQ_RENORM_EXEC 1
 #endif
@@ -192,95 +189,89 @@ __device__ __forceinline__ void raise_flag(uint32_t *status, uint32_t bits, uint
     if (status && bits && lane == 0) atomicOr(status, bits);
 }
 
+// Inclusive prefix sum / prefix maximum over the 64 lanes with DPP moves
+// (row shifts, then the row broadcasts of lanes 15 and 31), no LDS traffic.
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_scan(uint32_t x) {
+    auto op = [](uint32_t a, uint32_t b) { return MAX ? (a > b ? a : b) : a + b; };
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false));  // row_shr:1
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false));  // row_shr:2
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false));  // row_shr:4
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false));  // row_shr:8
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false));  // row_bcast:15
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false));  // row_bcast:31
+    return x;
+}
+
 // Slot table of the tensor (or of one segment's table): for every slot in
 // [0, 4096) the byte s with cum[s] <= slot < cum[s] + f[s], as the entry
 // (f[s], s, slot - cum[s]). A one-symbol tensor never builds a table; a
 // one-symbol segment does, with f = 4096 in every entry.
-__device__ __forceinline__ void build_lut(const uint16_t *freq, LutEnt *lut, uint32_t *scr) {
-    const uint32_t tid = threadIdx.x;
-    uint32_t *cum = scr;  // [257]
-#if EQ_LUT_SCAN
-    // Every present byte s marks its first slot cum[s] with s + 1; the byte
-    // of a slot is then the running maximum of the marks up to it (present
-    // bytes have increasing cum). Each thread owns P consecutive slots.
-    constexpr uint32_t P = 4096u / kThreads;
-    static_assert(P * kThreads == 4096u, "slots per thread");
-    uint32_t *wmax = scr + 260;  // [kWaves]
-    // the marks live in the table's own memory: every thread reads its marks
-    // before the barrier that precedes the first table write
-    uint16_t *mark = reinterpret_cast<uint16_t *>(lut);  // [4096]
+// Each wave fills its own 4096 / kWaves slots with no workgroup barrier: it
+// computes the cumulative frequencies itself (a wave scan), every present
+// byte s whose first slot cum[s] lies in the wave's range marks it with
+// s + 1, and the byte of a slot is the running maximum of the marks up to it
+// (present bytes have increasing cum), started from the byte that owns the
+// range's first slot. wscr: the wave's own scratch (its ring, not yet in
+// use). The caller's barrier publishes the table to the other waves.
+constexpr uint32_t kSlotsPerWave = 4096u / kWaves;
+constexpr uint32_t kSlotsPerLane = kSlotsPerWave / 64u;
+static_assert(kSlotsPerLane * 64u * kWaves == 4096u && kSlotsPerLane % 8u == 0, "slots per lane");
+
+__device__ __forceinline__ void build_lut(const uint16_t *freq, LutEnt *lut, uint32_t *wscr) {
+    constexpr uint32_t P = kSlotsPerLane;
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t lo = (threadIdx.x >> 6) * kSlotsPerWave;  // the wave's first slot
+    uint32_t *cum = wscr;                                     // [257]
+    uint16_t *mark = reinterpret_cast<uint16_t *>(wscr + 260);  // [kSlotsPerWave]
+    // bytes 4 lane .. 4 lane + 3
+    const uint2 fv = reinterpret_cast<const uint2 *>(freq)[lane];
+    const uint32_t f[4] = {fv.x & 0xFFFFu, fv.x >> 16, fv.y & 0xFFFFu, fv.y >> 16};
+    const uint32_t sum = f[0] + f[1] + f[2] + f[3];
+    const uint32_t incl = wave_scan<false>(sum);
 #pragma unroll
-    for (uint32_t j = 0; j < P; ++j) mark[P * tid + j] = 0;
-    __syncthreads();
-#endif
-    if (tid < 64) {
-        uint32_t f[4];
-        uint32_t s = 0;
+    for (uint32_t j = 0; j < P; j += 8)
+        *reinterpret_cast<uint4 *>(mark + P * lane + j) = make_uint4(0, 0, 0, 0);
+    __builtin_amdgcn_wave_barrier();
+    uint32_t c = incl - sum, cs[4], carry = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f[i] = freq[4 * tid + i];
-            s += f[i];
+    for (int i = 0; i < 4; ++i) {
+        cs[i] = c;
+        const uint32_t sym1 = 4u * lane + (uint32_t)i + 1u;
+        if (f[i]) {
+            if (c >= lo && c < lo + kSlotsPerWave) mark[c - lo] = (uint16_t)sym1;
+            if (c <= lo) carry = sym1;  // the latest present byte starting at or before lo
         }
-        uint32_t incl = s;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t v = __shfl_up(incl, o, 64);
-            if (tid >= (uint32_t)o) incl += v;
-        }
-        uint32_t c = incl - s;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            cum[4 * tid + i] = c;
-#if EQ_LUT_SCAN
-            if (f[i] && c < 4096u) mark[c] = (uint16_t)(4 * tid + i + 1);
-#endif
-            c += f[i];
-        }
-        if (tid == 63) cum[256] = incl;
+        c += f[i];
     }
-    __syncthreads();
-#if EQ_LUT_SCAN
+    *reinterpret_cast<uint4 *>(cum + 4u * lane) = make_uint4(cs[0], cs[1], cs[2], cs[3]);
+    if (lane == 63u) cum[256] = incl;
+    carry = (uint32_t)__builtin_amdgcn_readlane((int)wave_scan<true>(carry), 63);
+    __builtin_amdgcn_wave_barrier();
     uint32_t run[P];
     uint32_t m = 0;
 #pragma unroll
-    for (uint32_t j = 0; j < P; ++j) {
-        const uint32_t v = mark[P * tid + j];
-        m = v > m ? v : m;
-        run[j] = m;
-    }
-    // exclusive running maximum over the threads before this one
-    const uint32_t lane = tid & 63u, wave = tid >> 6;
-    uint32_t incl = m;
+    for (uint32_t j = 0; j < P; j += 8) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(mark + P * lane + j);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t v = __shfl_up(incl, o, 64);
-        if (lane >= (uint32_t)o) incl = v > incl ? v : incl;
+        for (uint32_t k = 0; k < 8; ++k) {
+            const uint32_t mk = (w[k / 2] >> (16u * (k % 2))) & 0xFFFFu;
+            m = mk > m ? mk : m;
+            run[j + k] = m;
+        }
     }
-    uint32_t before = __shfl_up(incl, 1, 64);
-    if (lane == 0) before = 0;
-    if (lane == 63) wmax[wave] = incl;
-    __syncthreads();
-    for (uint32_t w = 0; w < wave; ++w) before = wmax[w] > before ? wmax[w] : before;
+    // the running maximum of the lanes before this one (wave_shr:1), and the
+    // byte owning the range's first slot
+    uint32_t before = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)wave_scan<true>(m), 0x138, 0xF, 0xF, false);
+    before = before > carry ? before : carry;
 #pragma unroll
     for (uint32_t j = 0; j < P; ++j) {
-        const uint32_t slot = P * tid + j;
+        const uint32_t slot = lo + P * lane + j;
         const uint32_t sym = (run[j] > before ? run[j] : before) - 1u;
         const uint32_t c0 = cum[sym];
         lut[slot] = make_ent(sym, cum[sym + 1] - c0, slot - c0);
     }
-#else
-    for (uint32_t slot = tid; slot < 4096u; slot += kThreads) {
-        uint32_t lo = 0, hi = 256;  // cum[lo] <= slot < cum[hi]
-#pragma unroll
-        for (int it = 0; it < 8; ++it) {
-            const uint32_t mid = (lo + hi) >> 1;
-            if (cum[mid] <= slot) lo = mid; else hi = mid;
-        }
-        const uint32_t f = cum[lo + 1] - cum[lo];
-        lut[slot] = make_ent(lo, f, slot - cum[lo]);
-    }
-#endif
-    __syncthreads();
 }
 
 // Huffman decoding table of the tensor (codec 1), 4096 four-byte entries in
@@ -956,7 +947,8 @@ k_decode(LArgs a) {
     __shared__ LutEnt lut[4096];
     __shared__ __attribute__((aligned(16))) uint16_t rings[kWaves][kRingAlloc];
     // the slot-table build's scratch (cum, wave maxima) lives in the rings
-    static_assert(sizeof(rings) >= (260 + kWaves) * 4, "rings too small for the table build");
+    static_assert(sizeof(rings[0]) >= 260 * 4 + 2 * kSlotsPerWave, "a ring holds its wave's table-build scratch");
+    static_assert(sizeof(rings) >= (256 + 16 * 3) * 4, "the rings hold the Huffman table build's scratch");
 
     const uint32_t wg = blockIdx.x;
     uint32_t ti = 0;
@@ -969,16 +961,20 @@ k_decode(LArgs a) {
     // the LUT build's cumulative-frequency scratch reuses the (not yet
     // filled) rings
     if (!is_const) {
-        if (T.codec == eqfmt::kCodecHuffman)
+        if (T.codec == eqfmt::kCodecHuffman) {
             build_lut_huff(reinterpret_cast<const uint16_t *>(T.base + T.off_freq),
                            reinterpret_cast<uint32_t *>(lut), reinterpret_cast<uint32_t *>(&rings[0][0]));
-        else
+        } else {
             // the workgroup's chunks share one table (with adaptive tables the
-            // segment size is a multiple of the waves per workgroup)
+            // segment size is a multiple of the waves per workgroup); each
+            // wave builds its slice in its own ring's memory, then one
+            // barrier publishes the table
             build_lut(reinterpret_cast<const uint16_t *>(
                           T.base + T.off_freq +
                           (T.seg ? 512ull * (((uint64_t)(wg - T.wg_begin) * kWaves) / T.seg) : 0ull)),
-                      lut, reinterpret_cast<uint32_t *>(&rings[0][0]));
+                      lut, reinterpret_cast<uint32_t *>(&rings[wave][0]));
+            __syncthreads();
+        }
     }
     if (chunk >= T.n_chunks) return;
     if (is_const) {
