@@ -30,12 +30,29 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def host_cores() -> int:
+def host_cpus() -> dict:
+    """What the host offers: logical CPUs (os.cpu_count), those this process
+    may run on (affinity) and the CPU model (/proc/cpuinfo, as lscpu shows it)."""
     try:
-        n = len(os.sched_getaffinity(0))
+        aff = len(os.sched_getaffinity(0))
     except AttributeError:
-        n = os.cpu_count() or 1
-    return max(1, min(16, n))
+        aff = os.cpu_count() or 1
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "affinity": aff, "model": model}
+
+
+def host_cores() -> int:
+    """Threads for the CPU baseline: every CPU this process may use, capped at
+    16, the host share a one-GPU machine gives a job (whatever nproc reports)."""
+    return max(1, min(16, host_cpus()["affinity"]))
 
 
 def algorithmic_bytes(conts) -> tuple[int, int]:
@@ -154,6 +171,54 @@ def build_block(cfg: int, layer: int = 0, lane_run: int = 8, use_cache: bool = T
     return specs, conts
 
 
+class DeviceEncoder:
+    """Builds a block's containers on the device: codes drawn by the seeded
+    GPU sampler (the host sampler's values) and encoded by eq_encode_device;
+    each container is parsed on the host (its header) and kept on the device.
+    Buffers are sized for the largest tensor and reused."""
+
+    def __init__(self, specs, chunk: int, lane_run: int):
+        import torch
+        from rans_decode_amd import eq
+        self.Z, self.K = chunk, lane_run
+        self.sym = torch.empty(max(sp.n for sp in specs), dtype=torch.uint8, device="cuda")
+        self.ws = torch.empty(max(int(eq._lib.eq_encode_device_workspace(sp.rows, sp.cols, chunk)) for sp in specs),
+                              dtype=torch.uint8, device="cuda")
+        self.out = torch.empty(max(int(eq._lib.eq_encode_device_bound(sp.rows, sp.cols, chunk, sp.n_esc))
+                                   for sp in specs), dtype=torch.uint8, device="cuda")
+        self.d_len = torch.zeros(1, dtype=torch.int64, device="cuda")
+        self.d_st = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def container(self, cfg: int, layer: int, i: int, sp, Z: int | None = None):
+        import numpy as np
+        import torch
+        import synth
+        from rans_decode_amd import eq
+        Zc = Z or self.Z
+        need_ws = int(eq._lib.eq_encode_device_workspace(sp.rows, sp.cols, Zc))
+        need_out = int(eq._lib.eq_encode_device_bound(sp.rows, sp.cols, Zc, sp.n_esc))
+        if need_ws > self.ws.numel():
+            self.ws = torch.empty(need_ws, dtype=torch.uint8, device="cuda")
+        if need_out > self.out.numel():
+            self.out = torch.empty(need_out, dtype=torch.uint8, device="cuda")
+        sym = self.sym[:sp.n]
+        t = synth.make_tensor_gpu(cfg, layer, i, sym, spec=sp)
+        esc = t.esc_idx.size > 0
+        eq.eq_encode_device(sp.dtype, sp.rows, sp.cols, sym, torch.from_numpy(t.scales).cuda(),
+                            torch.from_numpy(t.esc_idx.astype(np.int64)).cuda() if esc else None,
+                            torch.from_numpy(t.esc_val.view(np.int16)).cuda() if esc else None,
+                            t.esc_code if esc else 0, Zc, self.K, workspace=self.ws, out=self.out,
+                            d_len=self.d_len, d_status=self.d_st)
+        n = int(self.d_len.item())
+        if int(self.d_st.item()):
+            raise RuntimeError(f"device encoder flagged config {cfg} layer {layer} tensor {i}")
+        c = eq.DeviceContainer.__new__(eq.DeviceContainer)
+        c.dev = self.out[:n].clone()
+        c.host = c.dev.cpu().numpy()
+        c.hdr = eq.parse_header(c.host)
+        return c
+
+
 def sampled_symbols_check(cfg, layer, specs, conts, rng_seed=1) -> int:
     """Decode-only pass (eq_decode_block, u8 codes) over the same containers;
     whole chunks (first, last and 3 random per tensor) are compared with the
@@ -234,30 +299,39 @@ def cpu_baseline(conts, target_s: float = 10.0):
         t1 += d
         m1 += m
     return {"value": round(2.0 * n / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": desc, "seconds": round(dt, 2),
+            "sample": desc, "seconds": round(dt, 2), "host": host_cpus(),
             "single_thread": {"value": round(2.0 * m1 / t1 / 1e9, 4), "unit": "GB/s", "cores": 1,
                               "sample": f"chunk 0 of each of the {len(conts)} tensor(s), {r1} pass(es)",
                               "seconds": round(t1, 2)}}
 
 
-def copy_ceiling(nbytes: int) -> float:
-    """GB/s (read + write) of a plain device-to-device copy of nbytes."""
+def copy_ceiling(nbytes: int) -> tuple[float, float]:
+    """GB/s (read + write) of a plain device-to-device copy of nbytes, and GB/s
+    of a read-only pass (an int64 sum) over the same nbytes. Both kernels also
+    serve as the known-size references that scale the HBM byte counters."""
     import torch
-    a = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda")
+    a = torch.ones(nbytes // 2, dtype=torch.int16, device="cuda")
     b = torch.empty_like(a)
     for _ in range(2):
         b.copy_(a)
+        a.sum(dtype=torch.int64)
     torch.cuda.synchronize()
+    reps = 10
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
-    reps = 10
     for _ in range(reps):
         b.copy_(a)
     e.record()
     torch.cuda.synchronize()
-    ms = s.elapsed_time(e) / reps
+    copy_ms = s.elapsed_time(e) / reps
+    s.record()
+    for _ in range(reps):
+        a.sum(dtype=torch.int64)
+    e.record()
+    torch.cuda.synchronize()
+    read_ms = s.elapsed_time(e) / reps
     del a, b
-    return 2.0 * nbytes / (ms * 1e-3) / 1e9
+    return 2.0 * nbytes / (copy_ms * 1e-3) / 1e9, nbytes / (read_ms * 1e-3) / 1e9
 
 
 CODECS = {"rans": 0, "huffman": 1}
@@ -343,6 +417,7 @@ def bench_block(args):
             "workload": f"{what}; {args.codec} codec, {Z // 1024} Ki-symbol chunks, 64 lanes, K={args.lane_run}, bf16 out"
                         + ("" if args.bits is None else f"; codes drawn at {args.bits:g} bits per weight"),
             "codec": args.codec,
+            "chunk_symbols": Z,
             "weights": n,
             "container_bytes": total_container,
             "effective_bits_per_weight": round(8.0 * total_container / n, 4),
@@ -357,8 +432,9 @@ def bench_block(args):
                      "traffic": traffic},
     }
     if not args.no_copy_ceiling:
-        cc = copy_ceiling(algo)
+        cc, rc = copy_ceiling(algo)
         rec["copy_ceiling_GBps"] = round(cc, 1)
+        rec["read_ceiling_GBps"] = round(rc, 1)
         rec["frac_of_copy_ceiling"] = round(achieved / cc, 4)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(conts, args.cpu_seconds)
@@ -713,9 +789,13 @@ def bench_model(args):
     t0 = time.perf_counter()
     blocks, xs, ys = [], [], []
     comp_bytes = 0
+    Z = args.chunk or synth.config_chunk(5)
+    enc = DeviceEncoder(specs, Z, args.lane_run)
     for layer in range(L):
-        _, conts = build_block(5, layer, args.lane_run, use_cache=False, chunk=args.chunk)
+        conts = [enc.container(5, layer, i, sp) for i, sp in enumerate(specs)]
         comp_bytes += algorithmic_bytes(conts)[0]
+        for c in conts:
+            c.host = None  # the header is parsed; the bytes stay on the device
         blocks.append(eq.Block(conts, offs[:-1], None))
         xs.append([torch.from_numpy(synth.gemv_activation(5, layer, i, sp.cols)).to(torch.bfloat16).cuda()
                    for i, sp in enumerate(specs)])
@@ -791,10 +871,11 @@ def bench_model(args):
     # whole-row chunks, the other six containers shared
     t1 = time.perf_counter()
     fblocks = []
+    zd = whole_row_chunk(specs[6].cols, args.lane_run, Z)
     for layer in range(L):
-        _, dconts = build_block(5, layer, args.lane_run, use_cache=False, tensors=[6], whole_rows=True,
-                                chunk=args.chunk)
-        fblocks.append(eq.Block(blocks[layer].containers[:6] + dconts, offs[:-1], None))
+        dc = enc.container(5, layer, 6, specs[6], Z=zd)
+        dc.host = None
+        fblocks.append(eq.Block(blocks[layer].containers[:6] + [dc], offs[:-1], None))
     log(f"whole-row down_proj containers built in {time.perf_counter() - t1:.0f} s")
     yf = [[torch.empty_like(y) for y in yl] for yl in ys]
 

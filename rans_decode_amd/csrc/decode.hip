@@ -775,10 +775,10 @@ struct Chunk {
     // (always inlined: an outlined copy would take the kernel argument's
     // address, which makes the compiler copy the whole argument block into
     // scratch memory)
-    __device__ __forceinline__ void run(uint64_t chunk, void *out, uint32_t *status) {
-        const uint8_t *dir = T.base + T.off_dir + chunk * 16u;
-        const uint64_t ws = *reinterpret_cast<const uint64_t *>(dir);
-        wc = *reinterpret_cast<const uint32_t *>(dir + 8);
+    // ws, wc_: the chunk's directory entry (first word, word count), loaded
+    // by the caller before the slot-table build
+    __device__ __forceinline__ void run(uint64_t chunk, void *out, uint32_t *status, uint64_t ws, uint32_t wc_) {
+        wc = wc_;
         wpad = (wc + 7u) & ~7u;
         if (wc > nk || ws + wpad > T.n_words) {
             raise_flag(status, EQ_DEV_WORD_OVERRUN, lane);
@@ -950,7 +950,14 @@ k_decode(LArgs a) {
     static_assert(sizeof(rings[0]) >= 260 * 4 + 2 * kSlotsPerWave, "a ring holds its wave's table-build scratch");
     static_assert(sizeof(rings) >= (256 + 16 * 3) * 4, "the rings hold the Huffman table build's scratch");
 
-    const uint32_t wg = blockIdx.x;
+    // Work item of this workgroup. The hardware hands workgroups to the 8
+    // XCDs in turn (block b to XCD b mod 8); the mapping below gives each XCD
+    // a contiguous run of work items instead, so the workgroups an XCD runs
+    // together read neighbouring chunks through its own L2 and write
+    // neighbouring stretches of the output (measured: -6% on the 70B block
+    // with 32 Ki chunks, -3% with 64 Ki).
+    const uint32_t G = gridDim.x, xcd = blockIdx.x & 7u, per = G >> 3, extra = G & 7u;
+    const uint32_t wg = xcd * per + (xcd < extra ? xcd : extra) + (blockIdx.x >> 3);
     uint32_t ti = 0;
     while (ti + 1 < a.n_tensors && wg >= a.t[ti + 1].wg_begin) ++ti;
     const TArgs &T = a.t[ti];
@@ -958,8 +965,15 @@ k_decode(LArgs a) {
     const uint32_t lane = threadIdx.x & 63u;
     const uint64_t chunk = (uint64_t)(wg - T.wg_begin) * kWaves + wave;
     const bool is_const = T.is_const != 0;
-    // the LUT build's cumulative-frequency scratch reuses the (not yet
-    // filled) rings
+    // the chunk's directory entry (scalar loads): in flight during the table build
+    uint64_t dir_ws = 0;
+    uint32_t dir_wc = 0;
+    if (!is_const && chunk < T.n_chunks) {
+        const uint8_t *dir = T.base + T.off_dir + chunk * 16u;
+        dir_ws = *reinterpret_cast<const uint64_t *>(dir);
+        dir_wc = *reinterpret_cast<const uint32_t *>(dir + 8);
+    }
+    // the table builds' scratch reuses the (not yet filled) rings
     if (!is_const) {
         if (T.codec == eqfmt::kCodecHuffman) {
             build_lut_huff(reinterpret_cast<const uint16_t *>(T.base + T.off_freq),
@@ -987,7 +1001,7 @@ k_decode(LArgs a) {
 #define EQ_RUN_C(BF, DT, MO, CO)                                                       \
     do {                                                                               \
         Chunk<K, BF, DT, MO, GEMV, CO> c{T, lut, rings[wave], lane, p0, nk};           \
-        c.run(chunk, a.out, a.status);                                                 \
+        c.run(chunk, a.out, a.status, dir_ws, dir_wc);                                                 \
     } while (0)
 #define EQ_RUN(BF, DT, MO)                                                             \
     do {                                                                               \
