@@ -306,15 +306,22 @@ def cpu_baseline(conts, target_s: float = 10.0):
 
 
 def copy_ceiling(nbytes: int) -> tuple[float, float]:
-    """GB/s (read + write) of a plain device-to-device copy of nbytes, and GB/s
-    of a read-only pass (an int64 sum) over the same nbytes. Both kernels also
-    serve as the known-size references that scale the HBM byte counters."""
+    """GB/s (read + write) of a plain device-to-device copy of nbytes (torch's
+    copy), and GB/s of a read-only pass over the same bytes: the library's
+    batch-1 GEMV (eq_gemv_bf16) over them as a bf16 [rows, 8192] matrix, which
+    reads each weight once (x and y are 16 KiB and rows x 4 B). Both kernels
+    are also the known-size references that scale the HBM byte counters."""
     import torch
-    a = torch.ones(nbytes // 2, dtype=torch.int16, device="cuda")
+    from rans_decode_amd import eq
+    cols = 8192
+    rows = nbytes // 2 // cols
+    a = torch.ones(rows * cols, dtype=torch.int16, device="cuda")
     b = torch.empty_like(a)
+    x = torch.ones(cols, dtype=torch.int16, device="cuda")
+    y = torch.empty(rows, dtype=torch.float32, device="cuda")
     for _ in range(2):
         b.copy_(a)
-        a.sum(dtype=torch.int64)
+        eq.eq_gemv_bf16(a, rows, cols, x, y)
     torch.cuda.synchronize()
     reps = 10
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -326,12 +333,12 @@ def copy_ceiling(nbytes: int) -> tuple[float, float]:
     copy_ms = s.elapsed_time(e) / reps
     s.record()
     for _ in range(reps):
-        a.sum(dtype=torch.int64)
+        eq.eq_gemv_bf16(a, rows, cols, x, y)
     e.record()
     torch.cuda.synchronize()
     read_ms = s.elapsed_time(e) / reps
     del a, b
-    return 2.0 * nbytes / (copy_ms * 1e-3) / 1e9, nbytes / (read_ms * 1e-3) / 1e9
+    return 2.0 * rows * cols * 2 / (copy_ms * 1e-3) / 1e9, rows * cols * 2 / (read_ms * 1e-3) / 1e9
 
 
 CODECS = {"rans": 0, "huffman": 1}
@@ -366,16 +373,13 @@ def bench_block(args):
     block = eq.Block(conts, offs[:-1], status)
     stream = torch.cuda.current_stream()
 
-    # one decode for the checks, then the warm-up right before the timed
-    # launches (an idle GPU between them would start the timing at low clocks)
+    # one decode and its status, the warm-up right before the timed launches,
+    # and the host-side decode check after them (an idle GPU between warm-up
+    # and timing would start the timing at low clocks)
     eq.eq_decode_dequant_bf16(block, out, stream)
     torch.cuda.synchronize()
     if int(status.item()) != 0:
         raise RuntimeError(f"device status {int(status.item())}")
-    bad = sampled_symbols_check(cfg, 0, specs, conts)
-    log(f"sampled decode check vs the generated symbols: {bad} mismatching codes")
-    if bad:
-        raise RuntimeError("decoded symbols differ from the encoded ones")
     for _ in range(args.warmup):
         eq.eq_decode_dequant_bf16(block, out, stream)
 
@@ -392,6 +396,10 @@ def bench_block(args):
     ms = [s.elapsed_time(e) for s, e in evs]
     if int(status.item()) != 0:
         raise RuntimeError(f"device status {int(status.item())}")
+    bad = sampled_symbols_check(cfg, 0, specs, conts)
+    log(f"sampled decode check vs the generated symbols: {bad} mismatching codes")
+    if bad:
+        raise RuntimeError("decoded symbols differ from the encoded ones")
     avg_ms = float(np.mean(ms))
     comp, outb = algorithmic_bytes(conts)
     algo = comp + outb
