@@ -380,6 +380,7 @@ def bench_block(args):
     torch.cuda.synchronize()
     if int(status.item()) != 0:
         raise RuntimeError(f"device status {int(status.item())}")
+    settle = clock_settle(lambda: eq.eq_decode_dequant_bf16(block, out, stream), stream, args.settle_ms)
     for _ in range(args.warmup):
         eq.eq_decode_dequant_bf16(block, out, stream)
 
@@ -438,6 +439,7 @@ def bench_block(args):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic},
+        "clock_settle": settle,
     }
     if not args.no_copy_ceiling:
         cc, rc = copy_ceiling(algo)
@@ -447,6 +449,27 @@ def bench_block(args):
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(conts, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
+
+
+def clock_settle(launch, stream, ms: float) -> dict:
+    """Back-to-back launches of the measured call for at least `ms` of GPU
+    time before the warm-up steps, untimed: an idle MI355X sits at ~160 MHz
+    and its clocks take tens of milliseconds of load to settle, longer than a
+    few warm-up launches of this kernel. Returns what ran (for the record)."""
+    import torch
+    if ms <= 0:
+        return {"launches": 0, "ms": 0.0}
+    n, total = 0, 0.0
+    while total < ms:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(10):
+            launch()
+        b.record(stream)
+        b.synchronize()
+        total += a.elapsed_time(b)
+        n += 10
+    return {"launches": n, "ms": round(total, 1)}
 
 
 def gemv_bound(w_bf16, x_bf16):
@@ -522,6 +545,7 @@ def bench_gemv(args):
             ms.append(s.elapsed_time(e))
         return ms
 
+    settle = clock_settle(lambda: eq.eq_decode_gemv_bf16(block, xs, ys, stream), stream, args.settle_ms)
     for _ in range(args.warmup):  # warm-up right before the timed launches
         eq.eq_decode_gemv_bf16(block, xs, ys, stream)
     wall0 = time.perf_counter()
@@ -563,6 +587,7 @@ def bench_gemv(args):
         "ratio_vs_bf16_resident": round(f / float(np.mean(gemv_ms)), 3),
         "roofline": roof,
         "fused_vs_unfused_worst_over_bound": round(worst, 5),
+        "clock_settle": settle,
     }
     print(json.dumps(rec), flush=True)
 
@@ -950,6 +975,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-ceiling", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="block workloads: untimed back-to-back launches for this much GPU time before "
+                         "the warm-up steps, so the timing starts at settled clocks (0: none)")
     ap.add_argument("--bits", type=float, default=None,
                     help="block workloads: entropy of the synthetic codes in bits per weight "
                          "(default: the configuration's)")

@@ -158,6 +158,33 @@ __device__ __forceinline__ XRun<K> load_x(const uint16_t *x) {
     return r;
 }
 
+// The same K inputs from global memory at base + off bytes, with base
+// wave-uniform (so the load takes a scalar base register and the lane's
+// 32-bit offset).
+template <int K>
+__device__ __forceinline__ XRun<K> load_x_global(uint64_t base, uint32_t off) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(1))) const uint8_t gbyte;
+    gbyte *p = reinterpret_cast<gbyte *>(base) + off;
+    XRun<K> r;
+    if constexpr (K == 1) {
+        r.p[0] = *reinterpret_cast<__attribute__((address_space(1))) const uint16_t *>(p);
+    } else if constexpr (K == 2) {
+        r.p[0] = *reinterpret_cast<__attribute__((address_space(1))) const uint32_t *>(p);
+    } else if constexpr (K == 4) {
+        const u32x2 v = *reinterpret_cast<__attribute__((address_space(1))) const u32x2 *>(p);
+        r.p[0] = v.x; r.p[1] = v.y;
+    } else {
+#pragma unroll
+        for (int i = 0; i < K / 8; ++i) {
+            const u32x4 v = reinterpret_cast<__attribute__((address_space(1))) const u32x4 *>(p)[i];
+            r.p[4 * i] = v.x; r.p[4 * i + 1] = v.y; r.p[4 * i + 2] = v.z; r.p[4 * i + 3] = v.w;
+        }
+    }
+    return r;
+}
+
 // 8-byte slot-table entry: lo = f | symbol << 24, hi = slot - cum. f is at
 // most 4096 (a segment of an adaptive-table container can hold one symbol),
 // so it fits bits 0..12 and bits 13..23 are zero: a 24-bit multiply by lo
@@ -539,14 +566,23 @@ struct Chunk {
         if constexpr (GEMV) {
             // the run's inputs, fetched before the K steps hide their latency
             // (a lane's run lies in one row; lanes past the chunk load nothing)
-            uint32_t c;
             if constexpr (MODE == M_ROW1) {
-                c = col + lane * (uint32_t)K;
+                if (!MASKED) {
+                    // a full group: every lane's run is inside the row; the
+                    // group's inputs start at a wave-uniform address (scalar
+                    // base + the lane's constant offset, no VALU address or
+                    // validity work)
+                    const uint64_t b = reinterpret_cast<uint64_t>(xv + col);
+                    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+                    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+                    xr = load_x_global<K>(((uint64_t)hi << 32) | (uint64_t)lo, lane * (uint32_t)(2 * K));
+                } else if (q0 < nk) {
+                    xr = load_x<K>(xv + col + lane * (uint32_t)K);
+                }
             } else {
                 rl = q0 / cols32;
-                c = q0 - rl * cols32;
+                if (q0 < nk) xr = load_x<K>(xv + (q0 - rl * cols32));
             }
-            if (q0 < nk) xr = load_x<K>(xv + c);
         }
         uint32_t ent[K];
 #pragma unroll
@@ -555,7 +591,7 @@ struct Chunk {
             ent[k] = step<MASKED>(q0 + (uint32_t)k < nk);
         }
         if constexpr (GEMV) {
-            gemv_group(g0, q0, rl, ent, xr);
+            gemv_group<MASKED>(g0, q0, rl, ent, xr);
             return;
         }
         if constexpr (BF16) {
@@ -639,9 +675,10 @@ struct Chunk {
     // bf16 decode would store them (scale, RNE, super weights), dotted with
     // its K inputs; row-uniform groups keep a per-lane partial until the row
     // ends, other groups reduce every row they touch at once.
+    template <bool MASKED>
     __device__ __forceinline__ void gemv_group(uint32_t g0, uint32_t q0, uint32_t rl, const uint32_t *ent,
                                                const XRun<K> &xr) {
-        const bool valid = q0 < nk;
+        const bool valid = !MASKED || q0 < nk;
         float s;
         if constexpr (MODE == M_ROW1) {
             s = s_cur;
@@ -661,7 +698,8 @@ struct Chunk {
             float a = acc;
 #pragma unroll
             for (int i = 0; i < (K + 1) / 2; ++i) a = dot2_bf16(pk[i], xr.p[i], a);
-            acc = valid ? a : acc;
+            if constexpr (MASKED) acc = valid ? a : acc;
+            else acc = a;
             advance_row();
         } else {
             float d = 0.0f;
