@@ -305,11 +305,12 @@ def cpu_baseline(conts, target_s: float = 10.0):
                               "seconds": round(t1, 2)}}
 
 
-def copy_ceiling(nbytes: int) -> tuple[float, float]:
+def copy_ceiling(nbytes: int) -> tuple[float, float, float]:
     """GB/s (read + write) of a plain device-to-device copy of nbytes (torch's
-    copy), and GB/s of a read-only pass over the same bytes: the library's
-    batch-1 GEMV (eq_gemv_bf16) over them as a bf16 [rows, 8192] matrix, which
-    reads each weight once (x and y are 16 KiB and rows x 4 B). Both kernels
+    copy), GB/s of a read-only pass over the same bytes (the library's batch-1
+    GEMV, eq_gemv_bf16, over them as a bf16 [rows, 8192] matrix, which reads
+    each weight once; x and y are 16 KiB and rows x 4 B), and GB/s of a
+    write-only pass (torch's fill of the same bytes). The copy and the GEMV
     are also the known-size references that scale the HBM byte counters."""
     import torch
     from rans_decode_amd import eq
@@ -322,23 +323,25 @@ def copy_ceiling(nbytes: int) -> tuple[float, float]:
     for _ in range(2):
         b.copy_(a)
         eq.eq_gemv_bf16(a, rows, cols, x, y)
+        b.fill_(3)
     torch.cuda.synchronize()
     reps = 10
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
-    for _ in range(reps):
-        b.copy_(a)
-    e.record()
-    torch.cuda.synchronize()
-    copy_ms = s.elapsed_time(e) / reps
-    s.record()
-    for _ in range(reps):
-        eq.eq_gemv_bf16(a, rows, cols, x, y)
-    e.record()
-    torch.cuda.synchronize()
-    read_ms = s.elapsed_time(e) / reps
+
+    def per_call(fn):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / reps
+
+    copy_ms = per_call(lambda: b.copy_(a))
+    read_ms = per_call(lambda: eq.eq_gemv_bf16(a, rows, cols, x, y))
+    write_ms = per_call(lambda: b.fill_(3))
     del a, b
-    return 2.0 * rows * cols * 2 / (copy_ms * 1e-3) / 1e9, rows * cols * 2 / (read_ms * 1e-3) / 1e9
+    nb = rows * cols * 2
+    return 2.0 * nb / (copy_ms * 1e-3) / 1e9, nb / (read_ms * 1e-3) / 1e9, nb / (write_ms * 1e-3) / 1e9
 
 
 CODECS = {"rans": 0, "huffman": 1}
@@ -397,6 +400,7 @@ def bench_block(args):
     ms = [s.elapsed_time(e) for s, e in evs]
     if int(status.item()) != 0:
         raise RuntimeError(f"device status {int(status.item())}")
+    u8_ms = decode_only_ms(block, n, stream, args.steps)
     bad = sampled_symbols_check(cfg, 0, specs, conts)
     log(f"sampled decode check vs the generated symbols: {bad} mismatching codes")
     if bad:
@@ -440,15 +444,38 @@ def bench_block(args):
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic},
         "clock_settle": settle,
+        "decode_only_u8": {"kernel_ms": round(u8_ms, 4),
+                           "frac": round((comp + n) / (u8_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                           "note": "eq_decode_block over the same containers (u8 codes out, n bytes written), "
+                                   "timed right after the bf16 launches"},
     }
     if not args.no_copy_ceiling:
-        cc, rc = copy_ceiling(algo)
+        cc, rc, wc = copy_ceiling(algo)
         rec["copy_ceiling_GBps"] = round(cc, 1)
         rec["read_ceiling_GBps"] = round(rc, 1)
+        rec["write_ceiling_GBps"] = round(wc, 1)
         rec["frac_of_copy_ceiling"] = round(achieved / cc, 4)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(conts, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
+
+
+def decode_only_ms(block, n: int, stream, steps: int) -> float:
+    """Mean kernel time of eq_decode_block (u8 codes out) over the block's
+    containers, `steps` launches back to back right after the bf16 timing."""
+    import numpy as np
+    import torch
+    from rans_decode_amd import eq
+    sym = torch.empty(n, dtype=torch.uint8, device="cuda")
+    eq.eq_decode_block(block, sym, stream)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for s, e in evs:
+        s.record(stream)
+        eq.eq_decode_block(block, sym, stream)
+        e.record(stream)
+    torch.cuda.synchronize()
+    del sym
+    return float(np.mean([s.elapsed_time(e) for s, e in evs]))
 
 
 def clock_settle(launch, stream, ms: float) -> dict:

@@ -158,27 +158,27 @@ __device__ __forceinline__ XRun<K> load_x(const uint16_t *x) {
     return r;
 }
 
-// The same K inputs from global memory at base + off bytes, with base
-// wave-uniform (so the load takes a scalar base register and the lane's
-// 32-bit offset).
+// The same K inputs through a buffer resource over the input vector: the
+// lane's constant byte offset in a VGPR and the group's wave-uniform byte
+// offset in an SGPR (no per-group VALU address work); bytes past the
+// resource's end read as zero.
+constexpr int kRawBufferWord3 = 0x00020000;  // raw (untyped) buffer, 32-bit data format
 template <int K>
-__device__ __forceinline__ XRun<K> load_x_global(uint64_t base, uint32_t off) {
+__device__ __forceinline__ XRun<K> load_x_buffer(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff) {
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    typedef __attribute__((address_space(1))) const uint8_t gbyte;
-    gbyte *p = reinterpret_cast<gbyte *>(base) + off;
     XRun<K> r;
     if constexpr (K == 1) {
-        r.p[0] = *reinterpret_cast<__attribute__((address_space(1))) const uint16_t *>(p);
+        r.p[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)voff, (int)soff, 0);
     } else if constexpr (K == 2) {
-        r.p[0] = *reinterpret_cast<__attribute__((address_space(1))) const uint32_t *>(p);
+        r.p[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)voff, (int)soff, 0);
     } else if constexpr (K == 4) {
-        const u32x2 v = *reinterpret_cast<__attribute__((address_space(1))) const u32x2 *>(p);
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)voff, (int)soff, 0);
         r.p[0] = v.x; r.p[1] = v.y;
     } else {
 #pragma unroll
         for (int i = 0; i < K / 8; ++i) {
-            const u32x4 v = reinterpret_cast<__attribute__((address_space(1))) const u32x4 *>(p)[i];
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(voff + 16u * i), (int)soff, 0);
             r.p[4 * i] = v.x; r.p[4 * i + 1] = v.y; r.p[4 * i + 2] = v.z; r.p[4 * i + 3] = v.w;
         }
     }
@@ -439,6 +439,7 @@ struct Chunk {
     char *ob;             // output of the chunk's first symbol
     // fused GEMV (the chunk starts at a row boundary and holds whole rows)
     const uint16_t *xv;   // the tensor's input vector
+    __amdgpu_buffer_rsrc_t xrsrc;  // the same as a buffer resource (cols < 2^31 bf16)
     float *yv;            // the tensor's output vector
     uint64_t row0;        // first row of the chunk
     float acc;            // row-uniform groups: this lane's partial of the current row
@@ -572,10 +573,7 @@ struct Chunk {
                     // group's inputs start at a wave-uniform address (scalar
                     // base + the lane's constant offset, no VALU address or
                     // validity work)
-                    const uint64_t b = reinterpret_cast<uint64_t>(xv + col);
-                    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
-                    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
-                    xr = load_x_global<K>(((uint64_t)hi << 32) | (uint64_t)lo, lane * (uint32_t)(2 * K));
+                    xr = load_x_buffer<K>(xrsrc, lane * (uint32_t)(2 * K), col * 2u);
                 } else if (q0 < nk) {
                     xr = load_x<K>(xv + col + lane * (uint32_t)K);
                 }
@@ -847,6 +845,9 @@ struct Chunk {
         eval = reinterpret_cast<const uint16_t *>(T.base + T.off_esc_val);
         if constexpr (GEMV) {
             xv = T.x;
+            if constexpr (MODE == M_ROW1)
+                xrsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(T.x), (short)0,
+                                                          (int)(uint32_t)(T.cols * 2u), kRawBufferWord3);
             yv = T.y;
             row0 = p0 / cols;
             acc = 0.0f;
@@ -1229,7 +1230,7 @@ eq_status launch_block(const eq_block *b, void *out, const uint16_t *const *x, f
                     return EQ_EINVAL;
                 t.x = x[i];
                 t.y = y[i];
-                t.mode = h.cols % G == 0 ? M_ROW1 : M_GENERAL;
+                t.mode = (h.cols % G == 0 && h.cols < (1ull << 31)) ? M_ROW1 : M_GENERAL;
             } else {
                 const uint32_t vec = BF16 ? 2u * (K < 8 ? K : 8u) : K;  // bytes per store
                 const uint64_t elem = BF16 ? 2u : 1u;
