@@ -298,7 +298,7 @@ N_LAYERS_MODEL = 80
 # 4096x4096 matrix mandates 64 Ki; elsewhere the size is a container field,
 # chosen by measured decode time against the 256 B of lane states each chunk
 # adds: smaller chunks shorten the serial work of the last waves of a launch.
-CONFIG_CHUNK = {1: 8192, 2: 65536, 3: 16384, 4: 32768, 5: 32768}
+CONFIG_CHUNK = {1: 8192, 2: 65536, 3: 16896, 4: 32768, 5: 32768}
 
 
 def config_chunk(cfg: int) -> int:
