@@ -832,8 +832,10 @@ def bench_drift(args):
 
 def bench_model(args):
     """80 blocks of the 70B-shaped layer, resident as containers (about 18 GB);
-    each token pass decodes block b into bf16 buffer b % 2 on one stream
-    while the other stream runs block b-1's seven batch-1 GEMVs (eq_pipeline).
+    each token pass decodes block b into bf16 buffer b % 2 on one stream and
+    runs its seven batch-1 GEMVs on the other (eq_pipeline; timed in the
+    alternating mode, where the decode of block b + 1 follows the GEMVs of
+    block b, and in the overlapped mode, where it runs beside them).
     Also timed: the 80 decodes alone (sustained decode rate) and the 80 x 7
     GEMVs over all blocks resident in bf16 (137 GB), the uncompressed
     baseline the pages compare with."""
@@ -883,6 +885,25 @@ def bench_model(args):
         torch.cuda.synchronize()
         tok_ms.append(s.elapsed_time(e))
     y_pipe = [[y.clone() for y in yl] for yl in ys]
+
+    # the same schedule with each decode beside the previous block's GEMVs
+    pipe.set_mode(eq.EQ_PIPELINE_OVERLAP)
+    token()
+    torch.cuda.synchronize()
+    ovl_ms = []
+    for _ in range(args.steps):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(ds)
+        token()
+        gs.wait_stream(ds)
+        e.record(gs)
+        torch.cuda.synchronize()
+        ovl_ms.append(s.elapsed_time(e))
+    same_ovl = all(torch.equal(a.view(torch.int32), b.view(torch.int32))
+                   for al, bl in zip(y_pipe, ys) for a, b in zip(al, bl))
+    if not same_ovl:
+        raise RuntimeError("the overlapped schedule's GEMV outputs differ from the alternating one's")
+    pipe.set_mode(eq.EQ_PIPELINE_ALTERNATE)
 
     # decodes alone, back to back on one stream
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -973,7 +994,8 @@ def bench_model(args):
         "scaling": "weak", "vs_baseline": None, "dtype": "u32/f32", "data": "synthetic",
         "config": {"workload": f"{L} x 70B-shaped block (int8 2.1-bit, K={args.lane_run}) resident as "
                                "containers; double-buffered decode on one HIP stream, 7 bf16 GEMVs per "
-                               "block (batch 1, N(0,1) activations) on another",
+                               "block (batch 1, N(0,1) activations) on another, the streams taking turns "
+                               "(eq_pipeline's alternating mode)",
                    "layers": L, "resident_container_bytes": resident_bytes,
                    "resident_GiB": round(resident_bytes / 2 ** 30, 3),
                    "effective_bits_per_weight": round(8.0 * resident_bytes / (nblk * L), 4)},
@@ -982,6 +1004,7 @@ def bench_model(args):
         "bf16_resident_gemv_ms_per_token": round(res, 3),
         "slowdown_vs_bf16_resident": round(tok / res, 3),
         "token_ms_all": [round(x, 3) for x in tok_ms],
+        "overlapped_mode_ms_per_token": round(float(np.median(ovl_ms)), 3),
         "fused_decode_gemv_ms_per_token": round(fus, 3),
         "fused_ratio_vs_bf16_resident": round(fus / res, 3),
         "fused_speedup_vs_pipeline": round(tok / fus, 3),

@@ -345,12 +345,18 @@ eq_status eq_gemv_bf16(const uint16_t *d_w, uint64_t rows, uint64_t cols, const 
  * GEMVs on the other buffer; events gate buffer reuse.
  *
  * eq_pipeline_create makes a plan holding 2 * n_blocks + 1 HIP events (no
- * device memory). eq_pipeline_run enqueues one pass: decode_stream first
- * waits for everything already enqueued on gemv_stream (a previous run's
- * GEMVs may still read either buffer); then for block b, decode into
- * buf[b % 2] after the GEMVs of block b - 2 finished, then the GEMVs of
- * block b (tensor i: W = buf[b % 2] + tensors[i].out_offset, rows/cols from
- * its header, x = d_x[b][i], y = d_y[b][i]) after that decode. The last
+ * device memory), in mode EQ_PIPELINE_ALTERNATE. eq_pipeline_run enqueues
+ * one pass: decode_stream first waits for everything already enqueued on
+ * gemv_stream (a previous run's GEMVs may still read either buffer); then
+ * for block b, decode into buf[b % 2] after the GEMVs of block b - 1
+ * (EQ_PIPELINE_ALTERNATE: the streams take turns, each kernel has the GPU to
+ * itself) or of block b - 2 (EQ_PIPELINE_OVERLAP: the decode of block b runs
+ * beside the GEMVs of block b - 1; b - 2 was the last reader of its buffer),
+ * then the GEMVs of block b (tensor i: W = buf[b % 2] +
+ * tensors[i].out_offset, rows/cols from its header, x = d_x[b][i],
+ * y = d_y[b][i]) after that decode. Both modes give the same results. On
+ * MI355X the two HBM-bound kernels slow each other down when they share the
+ * GPU, so the alternating mode is the faster one there. The last
  * GEMVs are on gemv_stream: the y of a run are complete once gemv_stream
  * reaches the end of that run (an event recorded there, or a synchronise);
  * runs may be enqueued back to back without a synchronise.
@@ -358,7 +364,12 @@ eq_status eq_gemv_bf16(const uint16_t *d_w, uint64_t rows, uint64_t cols, const 
  * pointers (one per tensor). Errors: EQ_EINVAL, EQ_EHIP.
  */
 typedef struct eq_pipeline eq_pipeline;
+#define EQ_PIPELINE_ALTERNATE 0u
+#define EQ_PIPELINE_OVERLAP 1u
 eq_status eq_pipeline_create(uint32_t n_blocks, eq_pipeline **out);
+/* Selects the gating of later runs (EQ_PIPELINE_ALTERNATE or
+ * EQ_PIPELINE_OVERLAP). Errors: EQ_EINVAL (null plan, unknown mode). */
+eq_status eq_pipeline_set_mode(eq_pipeline *p, uint32_t mode);
 eq_status eq_pipeline_run(eq_pipeline *p, const eq_block *blocks, uint32_t n_blocks,
                           uint16_t *d_buf0, uint16_t *d_buf1, const uint16_t *const *const *d_x,
                           float *const *const *d_y, void *decode_stream, void *gemv_stream);

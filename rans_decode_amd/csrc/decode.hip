@@ -1261,6 +1261,7 @@ eq_status launch_block(const eq_block *b, void *out, const uint16_t *const *x, f
 
 struct eq_pipeline {
     uint32_t n_blocks;
+    uint32_t overlap;  // EQ_PIPELINE_ALTERNATE or EQ_PIPELINE_OVERLAP
     std::vector<hipEvent_t> decoded, consumed;
     hipEvent_t start;  // gemv_stream's position when a run begins
 };
@@ -1307,6 +1308,7 @@ eq_status eq_pipeline_create(uint32_t n_blocks, eq_pipeline **out) {
     eq_pipeline *p = new (std::nothrow) eq_pipeline;
     if (!p) return EQ_ENOMEM;
     p->n_blocks = n_blocks;
+    p->overlap = EQ_PIPELINE_ALTERNATE;
     p->decoded.assign(n_blocks, nullptr);
     p->consumed.assign(n_blocks, nullptr);
     p->start = nullptr;
@@ -1326,6 +1328,12 @@ eq_status eq_pipeline_create(uint32_t n_blocks, eq_pipeline **out) {
     return EQ_OK;
 }
 
+eq_status eq_pipeline_set_mode(eq_pipeline *p, uint32_t mode) {
+    if (!p || (mode != EQ_PIPELINE_ALTERNATE && mode != EQ_PIPELINE_OVERLAP)) return EQ_EINVAL;
+    p->overlap = mode;
+    return EQ_OK;
+}
+
 eq_status eq_pipeline_run(eq_pipeline *p, const eq_block *blocks, uint32_t n_blocks,
                           uint16_t *d_buf0, uint16_t *d_buf1, const uint16_t *const *const *d_x,
                           float *const *const *d_y, void *decode_stream, void *gemv_stream) {
@@ -1337,9 +1345,13 @@ eq_status eq_pipeline_run(eq_pipeline *p, const eq_block *blocks, uint32_t n_blo
     // gemv_stream (a previous run's last blocks) may still be reading
     if (hipEventRecord(p->start, gs) != hipSuccess || hipStreamWaitEvent(ds, p->start, 0) != hipSuccess)
         return EQ_EHIP;
+    // the decode of block b waits for the GEMVs of block b - lag: b - 2 (the
+    // last reader of its buffer) when it may run beside the GEMVs of b - 1,
+    // b - 1 when the two streams take turns
+    const uint32_t lag = p->overlap == EQ_PIPELINE_OVERLAP ? 2u : 1u;
     for (uint32_t b = 0; b < n_blocks; ++b) {
         uint16_t *dst = buf[b & 1u];
-        if (b >= 2 && hipStreamWaitEvent(ds, p->consumed[b - 2], 0) != hipSuccess) return EQ_EHIP;
+        if (b >= lag && hipStreamWaitEvent(ds, p->consumed[b - lag], 0) != hipSuccess) return EQ_EHIP;
         eq_status st = eq_decode_dequant_bf16(&blocks[b], dst, ds);
         if (st != EQ_OK) return st;
         if (hipEventRecord(p->decoded[b], ds) != hipSuccess) return EQ_EHIP;

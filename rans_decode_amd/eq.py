@@ -30,6 +30,7 @@ EQ_DTYPE_INT8, EQ_DTYPE_E4M3 = 1, 2
 EQ_MAX_BLOCK_TENSORS = 16
 EQ_CODEC_RANS = 0
 EQ_CODEC_HUFFMAN = 1
+EQ_PIPELINE_ALTERNATE, EQ_PIPELINE_OVERLAP = 0, 1
 
 _u32, _u64, _i32, _vp = ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int32, ctypes.c_void_p
 
@@ -78,6 +79,7 @@ def _load():
         "eq_decode_gemv_bf16": [P(eq_block), _vp, _vp, _vp],
         "eq_gemv_bf16": [_vp, _u64, _u64, _vp, _vp, _vp],
         "eq_pipeline_create": [_u32, P(_vp)],
+        "eq_pipeline_set_mode": [_vp, _u32],
         "eq_pipeline_run": [_vp, P(eq_block), _u32, _vp, _vp, _vp, _vp, _vp, _vp],
         "eq_pipeline_destroy": [_vp],
         "eq_bf16_from_f32": [_vp, _u64, _vp, _vp],
@@ -311,12 +313,19 @@ def eq_bf16_from_f32(x, out, stream=None) -> None:
 
 class Pipeline:
     """eq_pipeline_*: blocks decoded into two alternating bf16 buffers on
-    decode_stream while gemv_stream runs each decoded block's GEMVs."""
+    decode_stream, each decoded block's GEMVs on gemv_stream; mode
+    EQ_PIPELINE_ALTERNATE (the default: the streams take turns) or
+    EQ_PIPELINE_OVERLAP (a decode runs beside the previous block's GEMVs)."""
 
-    def __init__(self, n_blocks: int):
+    def __init__(self, n_blocks: int, mode: int = None):
         self.h = _vp()
         _check("eq_pipeline_create", _lib.eq_pipeline_create(n_blocks, ctypes.byref(self.h)))
         self.n_blocks = n_blocks
+        if mode is not None:
+            self.set_mode(mode)
+
+    def set_mode(self, mode: int) -> None:
+        _check("eq_pipeline_set_mode", _lib.eq_pipeline_set_mode(self.h, mode))
 
     def run(self, blocks: list[Block], buf0, buf1, xs, ys, decode_stream, gemv_stream) -> None:
         n = len(blocks)

@@ -315,7 +315,8 @@ def test_gemv_matches_fp64_within_bound():
         assert np.all(np.abs(y.cpu().numpy() - ref) <= bound), (rows, cols)
 
 
-def test_pipeline_double_buffered_small_model():
+@pytest.mark.parametrize("mode", [eq.EQ_PIPELINE_ALTERNATE, eq.EQ_PIPELINE_OVERLAP])
+def test_pipeline_double_buffered_small_model(mode):
     """Block-by-block schedule on two streams (decode into alternating
     buffers, GEMVs on the other stream): every GEMV output equals the same
     GEMV over that block decoded into its own buffer, bit for bit, and every
@@ -338,7 +339,7 @@ def test_pipeline_double_buffered_small_model():
     n = offs[-1]
     bufs = [torch.empty(n, dtype=torch.bfloat16, device="cuda") for _ in range(2)]
     ds, gs = torch.cuda.Stream(), torch.cuda.Stream()
-    pipe = eq.Pipeline(L)
+    pipe = eq.Pipeline(L, mode)
     for _ in range(2):
         pipe.run(blocks, bufs[0], bufs[1], xs, ys, ds, gs)
     torch.cuda.synchronize()

@@ -23,6 +23,14 @@ def test_library_exports_every_declared_function():
         assert hasattr(lib, n), n
 
 
+def test_pipeline_mode_argument_checks():
+    """eq_pipeline_set_mode rejects a null plan before touching it (no HIP
+    call is made on this path)."""
+    lib = eq._lib
+    assert lib.eq_pipeline_set_mode(None, eq.EQ_PIPELINE_ALTERNATE) == eq.EQ_EINVAL
+    assert lib.eq_pipeline_set_mode(None, eq.EQ_PIPELINE_OVERLAP) == eq.EQ_EINVAL
+
+
 def test_struct_sizes_match_c_layout(tmp_path):
     """The binding's ctypes structs against the C compiler's view of eq.h."""
     import os
