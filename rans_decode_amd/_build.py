@@ -1,7 +1,8 @@
 """Compile libeq.so in-tree for gfx950.
 
-host_codec.cpp is plain C++17 (g++); decode.hip is HIP for gfx950 only
-(wave64, CDNA4), built without packed-fp32 instruction selection.
+host_codec.cpp is plain C++17 (g++); decode.hip and encode.hip are HIP for
+gfx950 only (wave64, CDNA4), built without packed-fp32 instruction
+selection; pipeline.hip is the host-side block schedule.
 """
 import os
 import subprocess
@@ -36,8 +37,11 @@ def build_library(verbose: bool = False, out: str = LIB, defines: dict | None = 
     enc_o = os.path.join(build_dir, "encode.o")
     _run(["hipcc", *HIPCC_FLAGS, *dflags, "-c", os.path.join(CSRC, "decode.hip"), "-o", dev_o], verbose)
     _run(["hipcc", *HIPCC_FLAGS, *dflags, "-c", os.path.join(CSRC, "encode.hip"), "-o", enc_o], verbose)
+    pipe_o = os.path.join(build_dir, "pipeline.o")
+    _run(["hipcc", *HIPCC_FLAGS, "-c", os.path.join(CSRC, "pipeline.hip"), "-o", pipe_o], verbose)
     tmp = out + ".tmp"
-    _run(["hipcc", "-shared", f"--offload-arch={ARCH}", host_o, dev_o, enc_o, "-o", tmp, "-pthread"], verbose)
+    _run(["hipcc", "-shared", f"--offload-arch={ARCH}", host_o, dev_o, enc_o, pipe_o, "-o", tmp, "-pthread"],
+         verbose)
     os.replace(tmp, out)
     return out
 
