@@ -296,8 +296,11 @@ N_LAYERS_MODEL = 80
 
 # Chunk size of each configuration's containers (symbols per chunk). The
 # 4096x4096 matrix mandates 64 Ki; elsewhere the size is a container field,
-# chosen by measured decode time against the 256 B of lane states each chunk
-# adds: smaller chunks shorten the serial work of the last waves of a launch.
+# chosen by measured decode time (compressed data read from HBM, not from the
+# last-level cache) against the 256 B of lane states each chunk adds: smaller
+# chunks shorten the serial work of the last waves of a launch. The fused
+# decode + GEMV wants longer chunks that hold whole rows (GEMV_CHUNK_TARGET).
+GEMV_CHUNK_TARGET = 32768
 CONFIG_CHUNK = {1: 8192, 2: 65536, 3: 16896, 4: 32768, 5: 32768}
 
 
