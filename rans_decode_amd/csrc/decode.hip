@@ -59,7 +59,9 @@ namespace {
 #define EQ_NT_STORES 1
 #endif
 #if EQ_NT_STORES
-#define EQ_NT_SUFFIX " nt"
+// non-temporal, system scope: with the compressed reads coming from HBM this
+// is 2.5% faster than non-temporal alone (0.389 vs 0.399 ms on the 70B block)
+#define EQ_NT_SUFFIX " nt sc1"
 #else
 #define EQ_NT_SUFFIX ""
 #endif
