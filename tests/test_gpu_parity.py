@@ -340,6 +340,8 @@ def test_pipeline_double_buffered_small_model(mode):
     bufs = [torch.empty(n, dtype=torch.bfloat16, device="cuda") for _ in range(2)]
     ds, gs = torch.cuda.Stream(), torch.cuda.Stream()
     pipe = eq.Pipeline(L, mode)
+    with pytest.raises(eq.EqError):
+        pipe.set_mode(2)  # unknown mode: EQ_EINVAL, the plan keeps its mode
     for _ in range(2):
         pipe.run(blocks, bufs[0], bufs[1], xs, ys, ds, gs)
     torch.cuda.synchronize()
