@@ -22,14 +22,25 @@ pytestmark = [pytest.mark.gpu,
 EXE = os.path.join(ROOT, "tests", "native", "c_consumer")
 
 
+def _ensure_exe():
+    """build() compiles the program; if this tree lacks it, compile it the
+    same way (one gcc call, host code only)."""
+    if os.path.exists(EXE):
+        return
+    subprocess.check_call(
+        ["gcc", "-std=c11", "-O2", "-D__HIP_PLATFORM_AMD__", "-I", "include", "-I", "/opt/rocm/include",
+         "tests/native/c_consumer.c", "-o", "tests/native/c_consumer", "-L", "rans_decode_amd", "-l:libeq.so",
+         "-Wl,-rpath,$ORIGIN/../../rans_decode_amd", "-L", "/opt/rocm/lib", "-lamdhip64",
+         "-Wl,-rpath,/opt/rocm/lib"], cwd=ROOT, timeout=120)
+
+
 @pytest.mark.parametrize("rows,cols,dtype,K,Z,codec,n_esc", [
     (64, 8192, synth.DTYPE_INT8, 8, 16384, 0, 4),      # rANS, super weights
     (37, 3000, synth.DTYPE_INT8, 1, 4096, 0, 0),       # ragged shape, K = 1, tail chunk
     (48, 4096, synth.DTYPE_E4M3, 4, 8192, 1, 3),       # Huffman, E4M3 escapes
 ])
 def test_c_consumer_matches_the_oracle(tmp_path, rows, cols, dtype, K, Z, codec, n_esc):
-    if not os.path.exists(EXE):
-        pytest.fail("tests/native/c_consumer is missing: run __graft_entry__.build() first")
+    _ensure_exe()
     spec = synth.TensorSpec("t", rows, cols, dtype, 2.1 if dtype == synth.DTYPE_INT8 else 2.3, n_esc)
     t = synth.make_tensor(4, 150 + K, 6, spec=spec)
     n = rows * cols
